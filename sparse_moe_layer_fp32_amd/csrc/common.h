@@ -1,0 +1,76 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, blocks are dealt round-robin
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) {
+  return __uint_as_float(packed & 0xFFFF0000u);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------------ math
+
+__device__ __forceinline__ float sigmoid_f32(float v) { return 1.0f / (1.0f + expf(-v)); }
+
+// SiLU(g) * u with the optional clamp: g <= L, -L <= u <= L when L > 0.
+__device__ __forceinline__ float swiglu_f32(float g, float u, float limit) {
+  if (limit > 0.0f) {
+    g = fminf(g, limit);
+    u = fminf(fmaxf(u, -limit), limit);
+  }
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// ------------------------------------------------------------------ MFMA
+// v_mfma_f32_32x32x16_bf16: A 32x16, B 16x32, C 32x32.  Lane l supplies row
+// (l % 32) of A and column (l % 32) of B, eight consecutive k each, lanes
+// 32..63 the upper eight.  C: lane l holds column l % 32, register r holds
+// row 8 * (r / 4) + 4 * (l / 32) + (r % 4).
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ int mfma32_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// ---------------------------------------------------------- XCD mapping
+// Blocks are dispatched to XCDs round-robin (block b -> XCD b % 8).  Given
+// `nvalid` units of work spread over `gridsize` blocks, give each XCD a
+// contiguous range of units so that blocks sharing operands share an L2.
+// Returns -1 for a block without work.
+__device__ __forceinline__ int xcd_remap(int bid, int gridsize, int nvalid) {
+  const int per = (nvalid + kNumXcd - 1) / kNumXcd;
+  const int xcd = bid % kNumXcd;
+  const int slot = bid / kNumXcd;
+  if (slot >= per) return -1;
+  const int u = xcd * per + slot;
+  (void)gridsize;
+  return u < nvalid ? u : -1;
+}
+
+}  // namespace moe

@@ -1,0 +1,338 @@
+// C ABI of libmoe.so: argument validation, workspace layout and the launch
+// sequence of the MoE layer forward.  Declarations and the contract of every
+// entry point are in include/moe.h.
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_error.clear();
+  return MOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Byte layout of the workspace for one configuration.
+struct Plan {
+  int64_t T, P;
+  int H, E, k, I, Is;
+  int S;         // router split-K factor
+  int C;         // permutation chunks
+  int tile_cap;  // capacity of the GEMM tile list
+  size_t zpart, ids, w, rank, hist, base, offsets, sorted, pos, tiles, ntiles, h, o, total;
+};
+
+moe_status validate(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->tokens < 0) return fail(MOE_ERR_INVALID_ARG, "tokens < 0 (%lld)", (long long)c->tokens);
+  if (c->hidden <= 0 || c->num_experts <= 0 || c->inter <= 0 || c->inter_shared < 0)
+    return fail(MOE_ERR_INVALID_ARG, "non-positive size (hidden %d, experts %d, inter %d, shared %d)",
+                c->hidden, c->num_experts, c->inter, c->inter_shared);
+  if (c->top_k < 1 || c->top_k > c->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k %d outside [1, num_experts=%d]", c->top_k,
+                c->num_experts);
+  if (c->num_experts > moe::kMaxExperts)
+    return fail(MOE_ERR_UNSUPPORTED, "num_experts %d > %d", c->num_experts, moe::kMaxExperts);
+  if (c->top_k > moe::kMaxTopK)
+    return fail(MOE_ERR_UNSUPPORTED, "top_k %d > %d", c->top_k, moe::kMaxTopK);
+  if (c->hidden % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden %d is not a multiple of 128", c->hidden);
+  if (c->inter % 64 || c->inter_shared % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "inter %d / inter_shared %d not multiples of 64", c->inter,
+                c->inter_shared);
+  if (c->tokens * static_cast<int64_t>(c->top_k) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "tokens * top_k must be < 2^31");
+  return MOE_OK;
+}
+
+void make_plan(const moe_config* c, Plan* p) {
+  p->T = c->tokens;
+  p->P = c->tokens * c->top_k;
+  p->H = c->hidden;
+  p->E = c->num_experts;
+  p->k = c->top_k;
+  p->I = c->inter;
+  p->Is = c->inter_shared;
+  const int T = static_cast<int>(p->T);
+  p->S = p->T > 0 ? moe::router_split(T, p->H, p->E) : 1;
+  p->C = static_cast<int>((p->P + moe::kPermuteChunk - 1) / moe::kPermuteChunk);
+  p->tile_cap = moe::experts_tile_capacity(p->T, static_cast<int>(p->P), p->E, p->Is > 0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t P = static_cast<size_t>(p->P), T64 = static_cast<size_t>(p->T);
+  p->zpart = take(static_cast<size_t>(p->S) * T64 * p->E * 4);
+  p->ids = take(P * 4);
+  p->w = take(P * 4);
+  p->rank = take(P * 4);
+  p->hist = take(static_cast<size_t>(p->E) * p->C * 4);
+  p->base = take(static_cast<size_t>(p->E) * p->C * 4);
+  p->offsets = take((static_cast<size_t>(p->E) + 1) * 4);
+  p->sorted = take(P * 4);
+  p->pos = take(P * 4);
+  p->tiles = take(static_cast<size_t>(p->tile_cap) * 8);
+  p->ntiles = take(16);
+  p->h = take((P * p->I + T64 * p->Is) * 2);
+  p->o = take((P + (p->Is > 0 ? T64 : 0)) * p->H * 2);
+  p->total = off;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MOE_CHECK_LAUNCH(expr, what)           \
+  do {                                         \
+    hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+moe_status check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  if (ws_bytes < p.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, p.total);
+  return MOE_OK;
+}
+
+moe_status route_impl(const Plan& p, const moe_config* c, const uint16_t* x, const float* rw,
+                      const float* rb, int32_t* ids, float* w, void* ws, hipStream_t stream,
+                      hipEvent_t* ev) {
+  float* zpart = at<float>(ws, p.zpart);
+  const int T = static_cast<int>(p.T);
+  if (ev) hipEventRecord(ev[0], stream);
+  MOE_CHECK_LAUNCH(moe::launch_router_gemm(x, rw, zpart, T, p.H, p.E, p.S, stream), "router gemm");
+  if (ev) hipEventRecord(ev[1], stream);
+  MOE_CHECK_LAUNCH(moe::launch_topk(zpart, p.S, rb, T, p.E, p.k, c->routed_scaling,
+                                    c->renormalize ? 1 : 0, ids, w, stream),
+                   "top-k");
+  return MOE_OK;
+}
+
+moe_status permute_impl(const Plan& p, const int32_t* ids, int32_t* offsets, int32_t* sorted,
+                        int32_t* pos, void* ws, hipStream_t stream, hipEvent_t* ev) {
+  MOE_CHECK_LAUNCH(
+      moe::launch_permute(ids, static_cast<int>(p.P), p.E, p.T, moe::experts_tile_rows(),
+                          p.Is > 0, at<int32_t>(ws, p.rank), at<int32_t>(ws, p.hist),
+                          at<int32_t>(ws, p.base), offsets, sorted, pos, at<int2>(ws, p.tiles),
+                          at<int32_t>(ws, p.ntiles), stream, ev),
+      "permute");
+  return MOE_OK;
+}
+
+moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* router_w,
+                        const float* router_bias, const uint16_t* w_gate, const uint16_t* w_up,
+                        const uint16_t* w_down, const uint16_t* ws_gate, const uint16_t* ws_up,
+                        const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
+                        float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                        hipEvent_t* ev) {
+  moe_status st = validate(c);
+  if (st) return st;
+  if (!router_w || !w_gate || !w_up || !w_down || (c->tokens > 0 && (!x || !y)))
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (c->inter_shared > 0 && (!ws_gate || !ws_up || !ws_down))
+    return fail(MOE_ERR_INVALID_ARG, "inter_shared > 0 but a shared-expert weight is NULL");
+  const void* ptrs[] = {x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                        y, topk_ids_out, topk_w_out};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MOE_ERR_UNSUPPORTED, "pointer %p not 16-byte aligned", q);
+  Plan p;
+  make_plan(c, &p);
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (p.T == 0) return ok();
+
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.ids);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, p.w);
+  int32_t* offsets = at<int32_t>(ws, p.offsets);
+  int32_t* sorted = at<int32_t>(ws, p.sorted);
+  int32_t* pos = at<int32_t>(ws, p.pos);
+  uint16_t* h_routed = at<uint16_t>(ws, p.h);
+  uint16_t* h_shared = h_routed + static_cast<size_t>(p.P) * p.I;
+  uint16_t* o_routed = at<uint16_t>(ws, p.o);
+  uint16_t* o_shared = p.Is > 0 ? o_routed + static_cast<size_t>(p.P) * p.H : nullptr;
+
+  if ((st = route_impl(p, c, x, router_w, router_bias, ids, w, ws, stream, ev))) return st;
+  if ((st = permute_impl(p, ids, offsets, sorted, pos, ws, stream, ev ? ev + 2 : nullptr)))
+    return st;
+
+  moe::GateUpArgs g{};
+  g.x = x;
+  g.sorted = sorted;
+  g.k = p.k;
+  g.T = p.T;
+  g.H = p.H;
+  g.w_gate = w_gate;
+  g.w_up = w_up;
+  g.I = p.I;
+  g.limit = c->swiglu_limit;
+  g.ws_gate = ws_gate;
+  g.ws_up = ws_up;
+  g.Is = p.Is;
+  g.limit_shared = c->swiglu_limit_shared;
+  g.tiles = at<int2>(ws, p.tiles);
+  g.ntiles = at<int32_t>(ws, p.ntiles);
+  g.offsets = offsets;
+  g.E = p.E;
+  g.h_routed = h_routed;
+  g.h_shared = h_shared;
+  g.NT = std::max(p.I, p.Is) / 64;
+  if (ev) hipEventRecord(ev[5], stream);
+  MOE_CHECK_LAUNCH(moe::launch_gateup(g, p.tile_cap, stream), "gate/up gemm");
+
+  moe::DownArgs d{};
+  d.h_routed = h_routed;
+  d.h_shared = h_shared;
+  d.w_down = w_down;
+  d.ws_down = ws_down;
+  d.H = p.H;
+  d.I = p.I;
+  d.Is = p.Is;
+  d.tiles = g.tiles;
+  d.ntiles = g.ntiles;
+  d.offsets = offsets;
+  d.E = p.E;
+  d.T = p.T;
+  d.sorted = sorted;
+  d.topk_w = w;
+  d.o_routed = o_routed;
+  d.o_shared = o_shared;
+  d.NT = p.H / 128;
+  if (ev) hipEventRecord(ev[6], stream);
+  MOE_CHECK_LAUNCH(moe::launch_down(d, p.tile_cap, stream), "down gemm");
+
+  if (ev) hipEventRecord(ev[7], stream);
+  MOE_CHECK_LAUNCH(moe::launch_combine(o_routed, o_shared, pos, p.k, p.T, p.H, y, stream),
+                   "combine");
+  if (ev) hipEventRecord(ev[8], stream);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  if (validate(cfg) != MOE_OK) return 0;
+  Plan p;
+  make_plan(cfg, &p);
+  return p.total;
+}
+
+const char* moe_last_error(void) { return g_error.c_str(); }
+
+moe_status moe_route(const moe_config* cfg, const uint16_t* x, const float* router_w,
+                     const float* router_bias, int32_t* topk_ids, float* topk_w, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  moe_status st = validate(cfg);
+  if (st) return st;
+  if (!router_w || (cfg->tokens > 0 && (!x || !topk_ids || !topk_w)))
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  const void* ptrs[] = {x, router_w, router_bias, topk_ids, topk_w};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MOE_ERR_UNSUPPORTED, "pointer %p not 16-byte aligned", q);
+  Plan p;
+  make_plan(cfg, &p);
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (p.T == 0) return ok();
+  if ((st = route_impl(p, cfg, x, router_w, router_bias, topk_ids, topk_w, ws, stream, nullptr)))
+    return st;
+  return ok();
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert_offsets,
+                       int32_t* sorted_pairs, int32_t* pair_pos, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status st = validate(cfg);
+  if (st) return st;
+  if (!expert_offsets || (cfg->tokens > 0 && (!topk_ids || !sorted_pairs || !pair_pos)))
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  const void* ptrs[] = {topk_ids, expert_offsets, sorted_pairs, pair_pos};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MOE_ERR_UNSUPPORTED, "pointer %p not 16-byte aligned", q);
+  Plan p;
+  make_plan(cfg, &p);
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (p.T == 0) {
+    // Offsets of an empty batch are all zero; nothing else to write.
+    MOE_CHECK_LAUNCH(moe::launch_fill_zero(expert_offsets, p.E + 1, stream), "zero offsets");
+    return ok();
+  }
+  if ((st = permute_impl(p, topk_ids, expert_offsets, sorted_pairs, pair_pos, ws, stream, nullptr)))
+    return st;
+  return ok();
+}
+
+moe_status moe_forward(const moe_config* cfg, const uint16_t* x, const float* router_w,
+                       const float* router_bias, const uint16_t* w_gate, const uint16_t* w_up,
+                       const uint16_t* w_down, const uint16_t* ws_gate, const uint16_t* ws_up,
+                       const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
+                       float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return forward_impl(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                      y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_timed(const moe_config* cfg, const uint16_t* x, const float* router_w,
+                             const float* router_bias, const uint16_t* w_gate,
+                             const uint16_t* w_up, const uint16_t* w_down,
+                             const uint16_t* ws_gate, const uint16_t* ws_up,
+                             const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
+                             float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                             hipEvent_t* events, int n_events) {
+  if (!events || n_events != MOE_NUM_STAGES + 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward_timed needs %d events", MOE_NUM_STAGES + 1);
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "event %d is NULL", i);
+  return forward_impl(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                      y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, events);
+}
+
+moe_status moe_workspace_view(const moe_config* cfg, int which, size_t* offset, size_t* bytes) {
+  moe_status st = validate(cfg);
+  if (st) return st;
+  if (!offset || !bytes) return fail(MOE_ERR_INVALID_ARG, "offset/bytes is NULL");
+  Plan p;
+  make_plan(cfg, &p);
+  const size_t P = static_cast<size_t>(p.P), T = static_cast<size_t>(p.T);
+  switch (which) {
+    case MOE_WS_TOPK_IDS: *offset = p.ids; *bytes = P * 4; break;
+    case MOE_WS_TOPK_W: *offset = p.w; *bytes = P * 4; break;
+    case MOE_WS_EXPERT_OFFSETS: *offset = p.offsets; *bytes = (static_cast<size_t>(p.E) + 1) * 4; break;
+    case MOE_WS_SORTED_PAIRS: *offset = p.sorted; *bytes = P * 4; break;
+    case MOE_WS_PAIR_POS: *offset = p.pos; *bytes = P * 4; break;
+    case MOE_WS_H: *offset = p.h; *bytes = (P * p.I + T * p.Is) * 2; break;
+    case MOE_WS_O: *offset = p.o; *bytes = (P + (p.Is > 0 ? T : 0)) * p.H * 2; break;
+    default: return fail(MOE_ERR_INVALID_ARG, "unknown workspace buffer id %d", which);
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,254 @@
+// Router of the MoE layer on gfx950: fp32 logits, sigmoid, bias used for
+// selection only, top-k with ties to the lower expert index, gating weights
+// renormalised over the selected experts and scaled.
+//
+// Follows the sglang-jax issue "[Feature] Support Step 3.5 Flash (StepFun)
+// Model", "Key difficulties" item 1, and the llm-atlas Step-3.5-Flash card's
+// raw config fields need_fp32_gate, moe_router_activation = sigmoid,
+// use_moe_router_bias, norm_expert_weight, moe_router_scaling_factor = 3.
+//
+// fp32 logits on bf16 matrix cores: x is bf16, and every fp32 router weight
+// w is split exactly into three bf16 terms w = hi + mid + lo (each step
+// rounds the remainder to the nearest bf16; 3 x 8 significand bits cover
+// fp32's 24).  Products of bf16 values are exact in fp32 and the MFMA
+// accumulates in fp32, so z = x.hi + x.mid + x.lo is an fp32 dot product of
+// the fp32 weights, at the bf16 MFMA rate.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int RT_BM = 64;   // tokens per tile
+constexpr int RT_BN = 64;   // experts per tile
+constexpr int RT_BK = 64;   // k per step
+constexpr int RT_LD = RT_BK + 8;  // padded LDS row (bf16 elements)
+
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f32_to_bf16_bits(w);
+  const float r1 = w - __uint_as_float(hi << 16);
+  mid = f32_to_bf16_bits(r1);
+  const float r2 = r1 - __uint_as_float(mid << 16);
+  lo = f32_to_bf16_bits(r2);
+}
+
+// zpart[s][t][e] = sum over k in split s of x[t][k] * wg[e][k].
+// Grid: (ceil(E/64), ceil(T/64), S); 256 threads = 4 waves in a 2x2 layout,
+// each wave one 32x32 output block.
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ wg,
+                                                          float* __restrict__ zpart, int T, int H,
+                                                          int E, int klen) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][RT_BM][RT_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][3][RT_BN][RT_LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int n0 = blockIdx.x * RT_BN;
+  const int m0 = blockIdx.y * RT_BM;
+  const int s = blockIdx.z;
+  const int kbeg = s * klen;
+  const int ksteps = klen / RT_BK;
+
+  // A: 64 rows x 64 bf16 = 512 16-byte chunks, 2 per thread.
+  const uint16_t* aptr[2];
+  bool aval[2];
+  int arow[2], acol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    arow[i] = c >> 3;
+    acol[i] = (c & 7) * 8;
+    const int t = m0 + arow[i];
+    aval[i] = t < T;
+    aptr[i] = x + static_cast<int64_t>(aval[i] ? t : 0) * H + kbeg + acol[i];
+  }
+  // B: 64 experts x 64 fp32 = 1024 16-byte chunks, 4 per thread.
+  const float* bptr[4];
+  bool bval[4];
+  int brow[4], bcol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    brow[i] = c >> 4;
+    bcol[i] = (c & 15) * 4;
+    const int e = n0 + brow[i];
+    bval[i] = e < E;
+    bptr[i] = wg + static_cast<int64_t>(bval[i] ? e : 0) * H + kbeg + bcol[i];
+  }
+
+  u32x4 ra[2];
+  f32x4 rb[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (aval[i]) v = *reinterpret_cast<const u32x4*>(aptr[i] + kt * RT_BK);
+      ra[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (bval[i]) v = *reinterpret_cast<const f32x4*>(bptr[i] + kt * RT_BK);
+      rb[i] = v;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(&sa[buf][arow[i]][acol[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split3(rb[i][q], hi[q], mid[q], lo[q]);
+      uint2 vh = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      uint2 vm = make_uint2(mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16));
+      uint2 vl = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+      *reinterpret_cast<uint2*>(&sb[buf][0][brow[i]][bcol[i]]) = vh;
+      *reinterpret_cast<uint2*>(&sb[buf][1][brow[i]][bcol[i]]) = vm;
+      *reinterpret_cast<uint2*>(&sb[buf][2][brow[i]][bcol[i]]) = vl;
+    }
+  };
+
+  f32x16 acc = {};
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int fr = lane & 31;
+  const int fk = (lane >> 5) * 8;
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ksteps) gload(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < RT_BK / 16; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sa[buf][32 * wm + fr][16 * ks + fk]);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const bf16x8 b =
+            *reinterpret_cast<const bf16x8*>(&sb[buf][p][32 * wn + fr][16 * ks + fk]);
+        acc = mfma32(a, b, acc);
+      }
+    }
+    if (kt + 1 < ksteps) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const int e = n0 + 32 * wn + fr;
+  if (e < E) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = m0 + 32 * wm + mfma32_row(r, lane);
+      if (t < T) zpart[(static_cast<int64_t>(s) * T + t) * E + e] = acc[r];
+    }
+  }
+}
+
+// One wave per token: sum the split partials in split order, sigmoid, key =
+// score + bias, k rounds of a wave-wide arg-max by (key desc, index asc),
+// then gating weights from the bias-free scores.
+constexpr int TK_MAX_SLOTS = 16;  // E <= 1024 = 16 slots x 64 lanes
+
+__device__ __forceinline__ bool ranks_before(float k1, int i1, float k2, int i2) {
+  return k1 > k2 || (k1 == k2 && i1 < i2);
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpart, int S,
+                                                   const float* __restrict__ bias, int T, int E,
+                                                   int k, float scaling, int renorm,
+                                                   int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nslots = (E + 63) >> 6;
+
+  float key[TK_MAX_SLOTS], sc[TK_MAX_SLOTS];
+#pragma unroll
+  for (int i = 0; i < TK_MAX_SLOTS; ++i) {
+    key[i] = -INFINITY;
+    sc[i] = 0.f;
+    const int e = lane + 64 * i;
+    if (i < nslots && e < E) {
+      float z = 0.f;
+      for (int s = 0; s < S; ++s) z += zpart[(static_cast<int64_t>(s) * T + t) * E + e];
+      sc[i] = sigmoid_f32(z);
+      key[i] = sc[i] + (bias ? bias[e] : 0.f);
+      if (key[i] != key[i]) key[i] = -INFINITY;  // non-finite input: rank last, stay in range
+    }
+  }
+
+  uint32_t taken = 0;
+  int my_id = 0;
+  float my_s = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bk = -INFINITY, bs = 0.f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < TK_MAX_SLOTS; ++i) {
+      const int e = lane + 64 * i;
+      if (i < nslots && e < E && !((taken >> i) & 1u) && ranks_before(key[i], e, bk, bi)) {
+        bk = key[i];
+        bi = e;
+        bs = sc[i];
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ok = __shfl_xor(bk, off);
+      const int oi = __shfl_xor(bi, off);
+      const float os = __shfl_xor(bs, off);
+      if (ranks_before(ok, oi, bk, bi)) {
+        bk = ok;
+        bi = oi;
+        bs = os;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) {
+      my_id = bi;
+      my_s = bs;
+    }
+  }
+  // Sum of the selected scores in slot order (lane 0 .. k-1).
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += __shfl(my_s, j);
+  if (lane < k) {
+    const float g = renorm ? my_s / sum : my_s;
+    ids[static_cast<int64_t>(t) * k + lane] = my_id;
+    w[static_cast<int64_t>(t) * k + lane] = g * scaling;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* zpart, int T, int H,
+                              int E, int S, hipStream_t stream) {
+  const dim3 grid((E + RT_BN - 1) / RT_BN, (T + RT_BM - 1) / RT_BM, S);
+  router_gemm_kernel<<<grid, 256, 0, stream>>>(x, wg, zpart, T, H, E, H / S);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* zpart, int S, const float* bias, int T, int E, int k,
+                       float scaling, int renorm, int32_t* ids, float* w, hipStream_t stream) {
+  const int blocks = (T + 3) / 4;
+  topk_kernel<<<blocks, 256, 0, stream>>>(zpart, S, bias, T, E, k, scaling, renorm, ids, w);
+  return hipGetLastError();
+}
+
+int router_split(int T, int H, int E) {
+  const int tiles = ((T + RT_BM - 1) / RT_BM) * ((E + RT_BN - 1) / RT_BN);
+  const int ksteps = H / RT_BK;
+  if (tiles >= 256) return 1;
+  int s = (512 + tiles - 1) / tiles;
+  if (s > 16) s = 16;
+  if (s > ksteps) s = ksteps;
+  while (s > 1 && ksteps % s) --s;
+  return s;
+}
+
+}  // namespace moe
