@@ -40,7 +40,8 @@
  *     (x, y, ids, weights, pair arrays) may then be NULL.
  *   - Limits: 1 <= top_k <= min(num_experts, 32); num_experts <= 1024;
  *     hidden % 128 == 0; inter % 64 == 0; inter_shared % 64 == 0 (0 = no
- *     shared expert); tokens * top_k < 2^31; every pointer 16-byte aligned.
+ *     shared expert); tokens * top_k < 2^31 and tokens * top_k *
+ *     max(hidden, inter, inter_shared) < 2^32; every pointer 16-byte aligned.
  *   - Preconditions not checked: inputs are finite; outputs do not alias
  *     inputs or the workspace; ids given to moe_permute are in [0, E).
  */

@@ -12,46 +12,33 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kPermuteChunk = 2048;  // pairs per rank/histogram chunk
 
-struct GateUpArgs {
-  const uint16_t* x;
-  const int32_t* sorted;
+// Arguments of the grouped expert GEMMs (gate/up and down share them).
+struct ExpertArgs {
+  const uint16_t* x;        // [T][H]
+  const int32_t* sorted;    // [P] pair ids in expert order
+  const float* topk_w;      // [T][k] gating weights (pair order)
   int k;
   int64_t T;
-  int H;
-  const uint16_t* w_gate;
-  const uint16_t* w_up;
-  int I;
-  float limit;
-  const uint16_t* ws_gate;
-  const uint16_t* ws_up;
-  int Is;
-  float limit_shared;
-  const int2* tiles;
-  const int32_t* ntiles;
-  const int32_t* offsets;
-  int E;
-  uint16_t* h_routed;  // [P][I]
-  uint16_t* h_shared;  // [T][Is]
-  int NT;              // 64-column tiles of max(I, Is)
+  int H, I, Is, E;
+  const uint16_t* w_gate;   // [E][I][H]
+  const uint16_t* w_up;     // [E][I][H]
+  const uint16_t* w_down;   // [E][H][I]
+  const uint16_t* ws_gate;  // [Is][H]
+  const uint16_t* ws_up;    // [Is][H]
+  const uint16_t* ws_down;  // [H][Is]
+  float limit, limit_shared;
+  const int2* tiles;        // (group, first row) per row tile; group E = shared
+  const int32_t* ntiles;    // number of valid tiles
+  const int32_t* offsets;   // [E+1]
+  uint16_t* h_routed;       // [P][I]
+  uint16_t* h_shared;       // [T][Is]
+  uint16_t* o_routed;       // [P][H]
+  uint16_t* o_shared;       // [T][H]
+  int NT;                   // column tiles (set by the launcher)
 };
 
-struct DownArgs {
-  const uint16_t* h_routed;
-  const uint16_t* h_shared;
-  const uint16_t* w_down;
-  const uint16_t* ws_down;
-  int H, I, Is;
-  const int2* tiles;
-  const int32_t* ntiles;
-  const int32_t* offsets;
-  int E;
-  int64_t T;
-  const int32_t* sorted;
-  const float* topk_w;
-  uint16_t* o_routed;  // [P][H]
-  uint16_t* o_shared;  // [T][H]
-  int NT;              // 128-column tiles of H
-};
+constexpr int kTileBig = 0;    // 256 x 256 tiles
+constexpr int kTileSmall = 1;  // 64 x 128 tiles
 
 // router.hip
 int router_split(int T, int H, int E);
@@ -69,10 +56,11 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, i
 hipError_t launch_fill_zero(int32_t* p, int n, hipStream_t stream);
 
 // experts.hip
-int experts_tile_rows();
-int experts_tile_capacity(int64_t T, int P, int E, int with_shared);
-hipError_t launch_gateup(const GateUpArgs& a, int tile_capacity, hipStream_t stream);
-hipError_t launch_down(const DownArgs& a, int tile_capacity, hipStream_t stream);
+int experts_pick_shape(int64_t T, int P, int E, int H, int I, int Is);
+int experts_tile_rows(int shape);
+int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape);
+hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream);
+hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* o_routed, const uint16_t* o_shared,
                           const int32_t* pair_pos, int k, int64_t T, int H, uint16_t* y,
                           hipStream_t stream);

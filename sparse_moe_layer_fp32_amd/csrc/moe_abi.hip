@@ -37,6 +37,7 @@ struct Plan {
   int H, E, k, I, Is;
   int S;         // router split-K factor
   int C;         // permutation chunks
+  int shape;     // expert GEMM tile shape (kTileBig / kTileSmall)
   int tile_cap;  // capacity of the GEMM tile list
   size_t zpart, ids, w, rank, hist, base, offsets, sorted, pos, tiles, ntiles, h, o, total;
 };
@@ -61,6 +62,9 @@ moe_status validate(const moe_config* c) {
                 c->inter_shared);
   if (c->tokens * static_cast<int64_t>(c->top_k) >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "tokens * top_k must be < 2^31");
+  if (c->tokens * static_cast<int64_t>(c->top_k) *
+          std::max<int64_t>(c->hidden, std::max(c->inter, c->inter_shared)) >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "tokens * top_k * max(hidden, inter) must be < 2^32");
   return MOE_OK;
 }
 
@@ -75,7 +79,8 @@ void make_plan(const moe_config* c, Plan* p) {
   const int T = static_cast<int>(p->T);
   p->S = p->T > 0 ? moe::router_split(T, p->H, p->E) : 1;
   p->C = static_cast<int>((p->P + moe::kPermuteChunk - 1) / moe::kPermuteChunk);
-  p->tile_cap = moe::experts_tile_capacity(p->T, static_cast<int>(p->P), p->E, p->Is > 0);
+  p->shape = moe::experts_pick_shape(p->T, static_cast<int>(p->P), p->E, p->H, p->I, p->Is);
+  p->tile_cap = moe::experts_tile_capacity(p->T, static_cast<int>(p->P), p->E, p->Is > 0, p->shape);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -141,7 +146,7 @@ moe_status route_impl(const Plan& p, const moe_config* c, const uint16_t* x, con
 moe_status permute_impl(const Plan& p, const int32_t* ids, int32_t* offsets, int32_t* sorted,
                         int32_t* pos, void* ws, hipStream_t stream, hipEvent_t* ev) {
   MOE_CHECK_LAUNCH(
-      moe::launch_permute(ids, static_cast<int>(p.P), p.E, p.T, moe::experts_tile_rows(),
+      moe::launch_permute(ids, static_cast<int>(p.P), p.E, p.T, moe::experts_tile_rows(p.shape),
                           p.Is > 0, at<int32_t>(ws, p.rank), at<int32_t>(ws, p.hist),
                           at<int32_t>(ws, p.base), offsets, sorted, pos, at<int2>(ws, p.tiles),
                           at<int32_t>(ws, p.ntiles), stream, ev),
@@ -184,50 +189,35 @@ moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* rou
   if ((st = permute_impl(p, ids, offsets, sorted, pos, ws, stream, ev ? ev + 2 : nullptr)))
     return st;
 
-  moe::GateUpArgs g{};
+  moe::ExpertArgs g{};
   g.x = x;
   g.sorted = sorted;
+  g.topk_w = w;
   g.k = p.k;
   g.T = p.T;
   g.H = p.H;
+  g.I = p.I;
+  g.Is = p.Is;
+  g.E = p.E;
   g.w_gate = w_gate;
   g.w_up = w_up;
-  g.I = p.I;
-  g.limit = c->swiglu_limit;
+  g.w_down = w_down;
   g.ws_gate = ws_gate;
   g.ws_up = ws_up;
-  g.Is = p.Is;
+  g.ws_down = ws_down;
+  g.limit = c->swiglu_limit;
   g.limit_shared = c->swiglu_limit_shared;
   g.tiles = at<int2>(ws, p.tiles);
   g.ntiles = at<int32_t>(ws, p.ntiles);
   g.offsets = offsets;
-  g.E = p.E;
   g.h_routed = h_routed;
   g.h_shared = h_shared;
-  g.NT = std::max(p.I, p.Is) / 64;
+  g.o_routed = o_routed;
+  g.o_shared = o_shared;
   if (ev) hipEventRecord(ev[5], stream);
-  MOE_CHECK_LAUNCH(moe::launch_gateup(g, p.tile_cap, stream), "gate/up gemm");
-
-  moe::DownArgs d{};
-  d.h_routed = h_routed;
-  d.h_shared = h_shared;
-  d.w_down = w_down;
-  d.ws_down = ws_down;
-  d.H = p.H;
-  d.I = p.I;
-  d.Is = p.Is;
-  d.tiles = g.tiles;
-  d.ntiles = g.ntiles;
-  d.offsets = offsets;
-  d.E = p.E;
-  d.T = p.T;
-  d.sorted = sorted;
-  d.topk_w = w;
-  d.o_routed = o_routed;
-  d.o_shared = o_shared;
-  d.NT = p.H / 128;
+  MOE_CHECK_LAUNCH(moe::launch_gateup(g, p.shape, p.tile_cap, stream), "gate/up gemm");
   if (ev) hipEventRecord(ev[6], stream);
-  MOE_CHECK_LAUNCH(moe::launch_down(d, p.tile_cap, stream), "down gemm");
+  MOE_CHECK_LAUNCH(moe::launch_down(g, p.shape, p.tile_cap, stream), "down gemm");
 
   if (ev) hipEventRecord(ev[7], stream);
   MOE_CHECK_LAUNCH(moe::launch_combine(o_routed, o_shared, pos, p.k, p.T, p.H, y, stream),
