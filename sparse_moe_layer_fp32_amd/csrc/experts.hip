@@ -31,7 +31,7 @@
 //    8 row tiles so that co-resident blocks share operands in their L2.
 //
 // Two tile shapes: 256 x 256 (one block per CU, 4 waves of 128 x 128) for
-// many rows per expert, and 64 x 128 with a 4-deep ring for few rows per
+// many rows per expert, and 64 x 128 with a 3-deep ring (two blocks per CU) for few rows per
 // expert, where the GEMMs stream weights at HBM rate.
 
 #include "common.h"
@@ -130,10 +130,13 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   else
     abase = shared ? a.h_shared : a.h_routed;
   uint32_t aoff[C::JA];
+  bool aon[C::JA];  // lanes of rows past the group's end load nothing (lane 0
+                    // re-reads row 0, so every DMA instruction is issued)
 #pragma unroll
   for (int j = 0; j < C::JA; ++j) {
     const int r = 8 * (wid * C::JA + j) + lrow;
-    const int rr = r < rows ? r : 0;  // rows past the group's end re-read row 0
+    aon[j] = r < rows || lane == 0;
+    const int rr = r < rows ? r : 0;
     int64_t src_row;
     if (MODE == 0) {
       src_row = shared ? static_cast<int64_t>(row0 + rr) : a.sorted[row0 + rr] / a.k;
@@ -166,7 +169,8 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     uint8_t* st = smem + (kt % S) * C::STAGE_BYTES;
     const int k0 = kt * BK;
 #pragma unroll
-    for (int j = 0; j < C::JA; ++j) dma16(abase + aoff[j] + k0, st + (wid * C::JA + j) * 1024);
+    for (int j = 0; j < C::JA; ++j)
+      if (aon[j]) dma16(abase + aoff[j] + k0, st + (wid * C::JA + j) * 1024);
 #pragma unroll
     for (int j = 0; j < C::JB; ++j)
       dma16(bsrc + static_cast<int64_t>(8 * j) * K + k0,
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 // Tile shapes.
 using BigTile = Cfg<256, 256, 2, 2, 2>;
-using SmallTile = Cfg<64, 128, 2, 2, 4>;
+using SmallTile = Cfg<64, 128, 2, 2, 3>;
 
 template <int MODE, int BM, int BN, int WM, int WN, int S>
 hipError_t launch_one(const ExpertArgs& a, int tile_capacity, int NT, hipStream_t stream) {
@@ -373,14 +377,14 @@ hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipS
   if (shape == kTileBig) {
     return launch_one<0, 256, 256, 2, 2, 2>(a, tile_capacity, (maxn + 127) / 128, stream);
   }
-  return launch_one<0, 64, 128, 2, 2, 4>(a, tile_capacity, (maxn + 63) / 64, stream);
+  return launch_one<0, 64, 128, 2, 2, 3>(a, tile_capacity, (maxn + 63) / 64, stream);
 }
 
 hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream) {
   if (shape == kTileBig) {
     return launch_one<1, 256, 256, 2, 2, 2>(a, tile_capacity, a.H / 256, stream);
   }
-  return launch_one<1, 64, 128, 2, 2, 4>(a, tile_capacity, a.H / 128, stream);
+  return launch_one<1, 64, 128, 2, 2, 3>(a, tile_capacity, a.H / 128, stream);
 }
 
 hipError_t launch_combine(const uint16_t* o_routed, const uint16_t* o_shared,

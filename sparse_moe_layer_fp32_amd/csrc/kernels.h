@@ -10,7 +10,6 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
-constexpr int kPermuteChunk = 2048;  // pairs per rank/histogram chunk
 
 // Arguments of the grouped expert GEMMs (gate/up and down share them).
 struct ExpertArgs {
@@ -54,6 +53,8 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, i
                           hipStream_t stream, hipEvent_t* ev);
 
 hipError_t launch_fill_zero(int32_t* p, int n, hipStream_t stream);
+int permute_chunk(int P);        // pairs per rank/histogram chunk (at most 64 chunks)
+int permute_hist_stride(int P);  // histogram row stride: chunk count rounded up to 4
 
 // experts.hip
 int experts_pick_shape(int64_t T, int P, int E, int H, int I, int Is);

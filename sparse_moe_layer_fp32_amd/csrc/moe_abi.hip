@@ -36,7 +36,7 @@ struct Plan {
   int64_t T, P;
   int H, E, k, I, Is;
   int S;         // router split-K factor
-  int C;         // permutation chunks
+  int C;         // permutation chunks, padded to a multiple of 4
   int shape;     // expert GEMM tile shape (kTileBig / kTileSmall)
   int tile_cap;  // capacity of the GEMM tile list
   size_t zpart, ids, w, rank, hist, base, offsets, sorted, pos, tiles, ntiles, h, o, total;
@@ -78,7 +78,7 @@ void make_plan(const moe_config* c, Plan* p) {
   p->Is = c->inter_shared;
   const int T = static_cast<int>(p->T);
   p->S = p->T > 0 ? moe::router_split(T, p->H, p->E) : 1;
-  p->C = static_cast<int>((p->P + moe::kPermuteChunk - 1) / moe::kPermuteChunk);
+  p->C = moe::permute_hist_stride(static_cast<int>(p->P));  // padded chunk count
   p->shape = moe::experts_pick_shape(p->T, static_cast<int>(p->P), p->E, p->H, p->I, p->Is);
   p->tile_cap = moe::experts_tile_capacity(p->T, static_cast<int>(p->P), p->E, p->Is > 0, p->shape);
   size_t off = 0;

@@ -1,17 +1,22 @@
 // Token permutation by expert: a stable counting sort of the (token, slot)
-// pairs by expert id, plus the tile lists of the grouped expert GEMMs.
+// pairs by expert id, plus the tile list of the grouped expert GEMMs.
 //
 // The grouping is what a grouped matmul over experts needs (sglang-jax issue
 // "[Feature] Support Step 3.5 Flash (StepFun) Model", "Implementation
 // strategy": grouped matmul first, checked against a per-expert loop).
 //
-// Three kernels, none with floating-point work and none order-dependent:
-//  rank     one wave per chunk of pairs: per-expert counts of the chunk and
-//           each pair's rank among the chunk's pairs of the same expert
-//           (wave ballots over the expert-id bits; pairs in ascending id).
-//  scan     one block: per-expert exclusive prefix over chunks, expert
-//           offsets (exclusive prefix over experts) and the GEMM tile list.
-//  scatter  position = offset[e] + chunk base[e] + rank.
+// The pairs are cut into spans.  Inside a span, one wave walks the pairs
+// in ascending id, 64 at a time: lanes holding the same expert find each
+// other by ballots over the bits of the expert id, so each pair gets its
+// rank among the chunk's earlier pairs of its expert and the chunk gets
+// per-expert counts.  An exclusive prefix over chunks (per expert) and over
+// experts then places every pair: position = offset[e] + base[e][c] + rank.
+// Nothing here depends on timing, so the permutation is deterministic.
+//
+// Chunks are ranked by whole blocks: each of 16 waves ranks a span of the
+// chunk and one thread per expert prefixes the waves' counts.  Small batches
+// (<= 4096 pairs) run all of it in one block; larger ones use three kernels
+// (rank, scan, scatter).
 
 #include "common.h"
 #include "kernels.h"
@@ -20,42 +25,52 @@ namespace moe {
 
 namespace {
 
-// hist is [E][C]: hist[e * C + c] = pairs of expert e in chunk c.
-__global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ ids, int P, int E,
-                                                  int chunk, int C, int32_t* __restrict__ rank,
-                                                  int32_t* __restrict__ hist) {
-  __shared__ int32_t cnt[kMaxExperts];
-  const int lane = threadIdx.x;
-  const int c = blockIdx.x;
-  for (int e = lane; e < E; e += 64) cnt[e] = 0;
-  __syncthreads();
+constexpr int kSmallPairs = 4096;
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Lanes of the wave holding the same expert id as this lane (valid lanes only).
+__device__ __forceinline__ uint64_t peers_of(int e, bool valid, int nbits) {
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    peers &= bit ? ones : ~ones;
+  }
+  return peers;
+}
+
+__device__ __forceinline__ int id_bits(int E) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  const int q0 = c * chunk;
-  const int q1 = min(P, q0 + chunk);
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  return nbits;
+}
+
+// Ranks of pairs [q0, q1) (ids staged in LDS at sid[q - q0]) among the
+// wave's earlier pairs of the same expert; cnt[e] carries the running count.
+// rank_out is indexed by q - rank_base.
+__device__ __forceinline__ void rank_span(const int32_t* sid, int q0, int q1, int E, int nbits,
+                                          int32_t* cnt, int32_t* rank_out, int rank_base) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lanes_below(lane);
   for (int q = q0; q < q1; q += 64) {
     const int p = q + lane;
-    const int e_in = p < q1 ? ids[p] : -1;
+    const int e_in = p < q1 ? sid[p - q0] : -1;
     const bool valid = e_in >= 0 && e_in < E;  // out-of-range ids are not counted
     const int e = valid ? e_in : 0;
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t ones = __ballot(valid && bit);
-      peers &= bit ? ones : ~ones;
-    }
+    const uint64_t peers = peers_of(e, valid, nbits);
     int base = 0;
     if (valid) base = cnt[e];
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     if (valid) {
-      rank[p] = base + __popcll(peers & below);
+      rank_out[p - rank_base] = base + __popcll(peers & below);
       const int leader = __ffsll(static_cast<unsigned long long>(peers)) - 1;
       if (lane == leader) cnt[e] = base + __popcll(peers);
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
   }
-  for (int e = lane; e < E; e += 64) hist[static_cast<int64_t>(e) * C + c] = cnt[e];
 }
 
 // Exclusive prefix sum over the 1024 threads of a block; returns the total
@@ -73,7 +88,7 @@ __device__ int block_excl_scan(int v, int* smem, int* total) {
   if (lane == 63) smem[wid] = incl;
   __syncthreads();
   if (wid == 0) {
-    int wv = lane < 16 ? smem[lane] : 0;
+    const int wv = lane < 16 ? smem[lane] : 0;
     int wincl = wv;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
@@ -90,57 +105,171 @@ __device__ int block_excl_scan(int v, int* smem, int* total) {
   return r;
 }
 
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist, int C, int E,
-                                                    int P, int64_t T, int bm, int with_shared,
-                                                    int32_t* __restrict__ base,
-                                                    int32_t* __restrict__ offsets,
-                                                    int2* __restrict__ tiles,
-                                                    int32_t* __restrict__ ntiles) {
-  __shared__ int32_t count[kMaxExperts];
-  __shared__ int smem[40];
+// Offsets from per-expert counts (one per thread, experts 0..E-1), then the
+// tile list: routed tiles expert by expert, then the shared expert's.
+__device__ void offsets_and_tiles(int count, int E, int64_t T, int bm, int with_shared,
+                                  int* smem, int32_t* offsets, int32_t* offs_lds,
+                                  int2* tiles, int32_t* ntiles) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  // Per-expert prefix over chunks (16 waves, one expert at a time each).
-  for (int e = wid; e < E; e += 16) {
-    int run = 0;
-    for (int c0 = 0; c0 < C; c0 += 64) {
-      const int c = c0 + lane;
-      const int v = c < C ? hist[static_cast<int64_t>(e) * C + c] : 0;
-      int incl = v;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (c < C) base[static_cast<int64_t>(e) * C + c] = run + incl - v;
-      run += __shfl(incl, 63);
-    }
-    if (lane == 0) count[e] = run;
-  }
-  __syncthreads();
-  // Expert offsets.
-  const int ce = tid < E ? count[tid] : 0;
   int tot = 0;
-  const int off = block_excl_scan(ce, smem, &tot);
-  if (tid < E) offsets[tid] = off;
+  const int off = block_excl_scan(tid < E ? count : 0, smem, &tot);
+  if (tid < E) {
+    offsets[tid] = off;
+    if (offs_lds) offs_lds[tid] = off;
+  }
   if (tid == 0) offsets[E] = tot;
-  // Tile list: routed tiles expert by expert, then the shared expert's.
-  const int nt = tid < E ? (ce + bm - 1) / bm : 0;
+  const int nt = tid < E ? (count + bm - 1) / bm : 0;
   int ntot = 0;
   const int tstart = block_excl_scan(nt, smem, &ntot);
   for (int i = 0; i < nt; ++i) tiles[tstart + i] = make_int2(tid, off + i * bm);
   const int nshared = with_shared ? static_cast<int>((T + bm - 1) / bm) : 0;
   for (int i = tid; i < nshared; i += 1024) tiles[ntot + i] = make_int2(E, i * bm);
   if (tid == 0) *ntiles = ntot + nshared;
-  (void)P;
+}
+
+// Ranks of the n <= kSmallPairs pairs staged in sid[0..n) among the earlier
+// pairs of the same expert: each of the 16 waves ranks a contiguous span,
+// then one thread per expert prefixes the waves' counts.  run[e] enters as
+// the count of pairs ranked before this span and leaves advanced; srank[q]
+// receives the rank.  wcnt must be zero on entry and is left zero.
+__device__ void block_rank(const int32_t* sid, int n, int E, int nbits,
+                           int32_t (*wcnt)[kMaxExperts], int32_t* run, int32_t* srank) {
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int CH = ((n + 15) / 16 + 63) / 64 * 64;  // pairs per wave
+  const int q0 = min(n, wid * CH), q1 = min(n, q0 + CH);
+  rank_span(sid + q0, q0, q1, E, nbits, wcnt[wid], srank, 0);
+  __syncthreads();
+  if (tid < E) {
+    int c = run[tid];
+    for (int w = 0; w < 16; ++w) {
+      const int t = wcnt[w][tid];
+      wcnt[w][tid] = c;
+      c += t;
+    }
+    run[tid] = c;
+  }
+  __syncthreads();
+  for (int q = tid; q < n; q += 1024) {
+    const int e = sid[q];
+    if (e >= 0 && e < E) srank[q] += wcnt[q / CH][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- small
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int64_t T, int bm, int with_shared,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
+    int2* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+  __shared__ int32_t sid[kSmallPairs];
+  __shared__ int32_t srank[kSmallPairs];
+  __shared__ int32_t wcnt[16][kMaxExperts];
+  __shared__ int32_t run[kMaxExperts];
+  __shared__ int smem[40];
+  const int tid = threadIdx.x;
+  for (int p = tid; p < P; p += 1024) sid[p] = ids[p];
+  for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
+  for (int e = tid; e < E; e += 1024) run[e] = 0;
+  __syncthreads();
+  block_rank(sid, P, E, id_bits(E), wcnt, run, srank);
+  const int count = tid < E ? run[tid] : 0;
+  offsets_and_tiles(count, E, T, bm, with_shared, smem, offsets, run, tiles, ntiles);
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024) {
+    const int e = sid[p];
+    if (e < 0 || e >= E) continue;
+    const int i = run[e] + srank[p];
+    sorted[i] = p;
+    pos[p] = i;
+  }
+}
+
+// ---------------------------------------------------------------- large
+
+// One block per chunk of pairs: ranks within the chunk and the chunk's
+// per-expert counts.  hist is [E][Cp]: hist[e * Cp + c] = pairs of expert e
+// in chunk c (rows padded to Cp, a multiple of 4, for 16-byte loads).
+__global__ __launch_bounds__(1024) void rank_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                    int chunk, int Cp, int32_t* __restrict__ rank,
+                                                    int32_t* __restrict__ hist) {
+  __shared__ int32_t sid[kSmallPairs];
+  __shared__ int32_t srank[kSmallPairs];
+  __shared__ int32_t wcnt[16][kMaxExperts];
+  __shared__ int32_t run[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x;
+  for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
+  for (int e = tid; e < E; e += 1024) run[e] = 0;
+  const int nbits = id_bits(E);
+  const int q_end = min(P, (c + 1) * chunk);
+  for (int q0 = c * chunk; q0 < q_end; q0 += kSmallPairs) {
+    const int n = min(q_end - q0, kSmallPairs);
+    int v[kSmallPairs / 1024];
+#pragma unroll
+    for (int i = 0; i < kSmallPairs / 1024; ++i) {
+      const int q = tid + 1024 * i;
+      v[i] = q < n ? ids[q0 + q] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kSmallPairs / 1024; ++i) sid[tid + 1024 * i] = v[i];
+    __syncthreads();
+    block_rank(sid, n, E, nbits, wcnt, run, srank);
+    for (int q = tid; q < n; q += 1024) rank[q0 + q] = srank[q];
+    __syncthreads();
+  }
+  for (int e = tid; e < E; e += 1024) hist[static_cast<int64_t>(e) * Cp + c] = run[e];
+}
+
+// One block, one thread per expert: the expert's chunk counts (C <= 64,
+// row stride Cp) come in with 16-byte loads, all in flight together, and
+// are prefixed in registers.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist, int C, int Cp,
+                                                    int E, int64_t T, int bm, int with_shared,
+                                                    int32_t* __restrict__ base,
+                                                    int32_t* __restrict__ offsets,
+                                                    int2* __restrict__ tiles,
+                                                    int32_t* __restrict__ ntiles) {
+  __shared__ int smem[40];
+  const int e = threadIdx.x;
+  int count = 0;
+  if (e < E) {
+    const int4* src = reinterpret_cast<const int4*>(hist + static_cast<int64_t>(e) * Cp);
+    int4* dst = reinterpret_cast<int4*>(base + static_cast<int64_t>(e) * Cp);
+    int4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (4 * i < C) {
+        int4 t = src[i];  // padding columns past C are not written by the rank kernel
+        if (4 * i + 1 >= C) t.y = 0;
+        if (4 * i + 2 >= C) t.z = 0;
+        if (4 * i + 3 >= C) t.w = 0;
+        v[i] = t;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (4 * i < C) {
+        int4 o;
+        o.x = count; count += v[i].x;
+        o.y = count; count += v[i].y;
+        o.z = count; count += v[i].z;
+        o.w = count; count += v[i].w;
+        dst[i] = o;
+      }
+    }
+  }
+  offsets_and_tiles(count, E, T, bm, with_shared, smem, offsets, nullptr, tiles, ntiles);
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids,
                                                       const int32_t* __restrict__ rank,
                                                       const int32_t* __restrict__ base,
                                                       const int32_t* __restrict__ offsets, int P,
-                                                      int E, int C, int chunk,
+                                                      int E, int Cp, int chunk,
                                                       int32_t* __restrict__ sorted,
                                                       int32_t* __restrict__ pos) {
   const int p = blockIdx.x * 256 + threadIdx.x;
@@ -148,7 +277,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int e = ids[p];
   if (e < 0 || e >= E) return;  // not counted by the rank kernel
   const int c = p / chunk;
-  const int i = offsets[e] + base[static_cast<int64_t>(e) * C + c] + rank[p];
+  const int i = offsets[e] + base[static_cast<int64_t>(e) * Cp + c] + rank[p];
   sorted[i] = p;
   pos[p] = i;
 }
@@ -160,6 +289,18 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, int n) {
 
 }  // namespace
 
+int permute_hist_stride(int P) {
+  const int chunk = permute_chunk(P);
+  const int C = (P + chunk - 1) / chunk;
+  return (C + 3) / 4 * 4;
+}
+
+int permute_chunk(int P) {
+  // At most 64 chunks, each a multiple of the LDS staging size.
+  const int per = (P + 63) / 64;
+  return std::max(kSmallPairs, (per + kSmallPairs - 1) / kSmallPairs * kSmallPairs);
+}
+
 hipError_t launch_fill_zero(int32_t* p, int n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   fill_zero_kernel<<<(n + 255) / 256, 256, 0, stream>>>(p, n);
@@ -170,19 +311,31 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, i
                           int32_t* rank, int32_t* hist, int32_t* base, int32_t* offsets,
                           int32_t* sorted, int32_t* pos, int2* tiles, int32_t* ntiles,
                           hipStream_t stream, hipEvent_t* ev) {
-  const int C = (P + kPermuteChunk - 1) / kPermuteChunk;
+  if (P <= kSmallPairs) {
+    if (ev) hipEventRecord(ev[0], stream);
+    permute_small_kernel<<<1, 1024, 0, stream>>>(ids, P, E, T, bm, with_shared, offsets, sorted,
+                                                 pos, tiles, ntiles);
+    if (ev) {
+      hipEventRecord(ev[1], stream);
+      hipEventRecord(ev[2], stream);
+    }
+    return hipGetLastError();
+  }
+  const int chunk = permute_chunk(P);
+  const int C = (P + chunk - 1) / chunk;
+  const int Cp = permute_hist_stride(P);
   if (ev) hipEventRecord(ev[0], stream);
-  rank_kernel<<<C, 64, 0, stream>>>(ids, P, E, kPermuteChunk, C, rank, hist);
+  rank_kernel<<<C, 1024, 0, stream>>>(ids, P, E, chunk, Cp, rank, hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev) hipEventRecord(ev[1], stream);
-  scan_kernel<<<1, 1024, 0, stream>>>(hist, C, E, P, T, bm, with_shared, base, offsets, tiles,
+  scan_kernel<<<1, 1024, 0, stream>>>(hist, C, Cp, E, T, bm, with_shared, base, offsets, tiles,
                                       ntiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev) hipEventRecord(ev[2], stream);
-  scatter_kernel<<<(P + 255) / 256, 256, 0, stream>>>(ids, rank, base, offsets, P, E, C,
-                                                      kPermuteChunk, sorted, pos);
+  scatter_kernel<<<(P + 255) / 256, 256, 0, stream>>>(ids, rank, base, offsets, P, E, Cp, chunk,
+                                                      sorted, pos);
   return hipGetLastError();
 }
 

@@ -34,13 +34,14 @@ __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uin
   lo = f32_to_bf16_bits(r2);
 }
 
-// zpart[s][t][e] = sum over k in split s of x[t][k] * wg[e][k].
+// zpart[t][e][s] = sum over k in split s of x[t][k] * wg[e][k] (the split
+// partials of one logit are contiguous, S in {1, 2, 4, 8}).
 // Grid: (ceil(E/64), ceil(T/64), S); 256 threads = 4 waves in a 2x2 layout,
 // each wave one 32x32 output block.
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wg,
                                                           float* __restrict__ zpart, int T, int H,
-                                                          int E, int klen) {
+                                                          int E, int klen, int nsplit) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[2][RT_BM][RT_LD];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][3][RT_BN][RT_LD];
 
@@ -143,80 +144,123 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = m0 + 32 * wm + mfma32_row(r, lane);
-      if (t < T) zpart[(static_cast<int64_t>(s) * T + t) * E + e] = acc[r];
+      if (t < T) zpart[(static_cast<int64_t>(t) * E + e) * nsplit + s] = acc[r];
     }
   }
 }
 
-// One wave per token: sum the split partials in split order, sigmoid, key =
-// score + bias, k rounds of a wave-wide arg-max by (key desc, index asc),
-// then gating weights from the bias-free scores.
+// One wave per token.  Lane l holds experts l, l+64, ...; each expert's
+// logit is the sum of the split partials in split order, its score the
+// fp32 sigmoid, its selection key score + bias.  Keys are packed with the
+// expert index into one orderable 64-bit word, (key, 2^32-1-index), so one
+// unsigned max picks the largest key and, among equal keys, the lower index.
+// k rounds of a wave-wide max (DPP within rows of 16 lanes, then the four
+// row results) select the experts in rank order; the winner's lane retires
+// it.  Gating weights come from the bias-free scores of the selected set.
 constexpr int TK_MAX_SLOTS = 16;  // E <= 1024 = 16 slots x 64 lanes
 
-__device__ __forceinline__ bool ranks_before(float k1, int i1, float k2, int i2) {
-  return k1 > k2 || (k1 == k2 && i1 < i2);
+__device__ __forceinline__ uint32_t orderable(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF,
+                                             0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(static_cast<int>(v >> 32),
+                                             static_cast<int>(v >> 32), CTRL, 0xF, 0xF, false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Wave-wide maximum, uniform result.  Within each row of 16 lanes: swap
+// neighbours, pairs, mirror halves of 8, mirror the row; then the rows.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp64<0xB1>(v);  v = o > v ? o : v;   // quad_perm [1,0,3,2]
+  o = dpp64<0x4E>(v);  v = o > v ? o : v;   // quad_perm [2,3,0,1]
+  o = dpp64<0x141>(v); v = o > v ? o : v;   // row_half_mirror
+  o = dpp64<0x140>(v); v = o > v ? o : v;   // row_mirror
+  const uint64_t r0 = readlane64(v, 0), r1 = readlane64(v, 16);
+  const uint64_t r2 = readlane64(v, 32), r3 = readlane64(v, 48);
+  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
+// Sum of the S split partials of one logit, in split order.
+__device__ __forceinline__ float sum_splits(const float* p, int S) {
+  if (S == 1) return p[0];
+  if (S == 2) {
+    const float2 a = *reinterpret_cast<const float2*>(p);
+    return a.x + a.y;
+  }
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  float acc = ((a[0] + a[1]) + a[2]) + a[3];
+  if (S == 8) {
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    acc = (((acc + b[0]) + b[1]) + b[2]) + b[3];
+  }
+  return acc;
+}
+
+template <int NS>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpart, int S,
                                                    const float* __restrict__ bias, int T, int E,
                                                    int k, float scaling, int renorm,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;
-  const int nslots = (E + 63) >> 6;
 
-  float key[TK_MAX_SLOTS], sc[TK_MAX_SLOTS];
+  float z[NS];
+  uint64_t key[NS];
 #pragma unroll
-  for (int i = 0; i < TK_MAX_SLOTS; ++i) {
-    key[i] = -INFINITY;
-    sc[i] = 0.f;
+  for (int i = 0; i < NS; ++i) {
     const int e = lane + 64 * i;
-    if (i < nslots && e < E) {
-      float z = 0.f;
-      for (int s = 0; s < S; ++s) z += zpart[(static_cast<int64_t>(s) * T + t) * E + e];
-      sc[i] = sigmoid_f32(z);
-      key[i] = sc[i] + (bias ? bias[e] : 0.f);
-      if (key[i] != key[i]) key[i] = -INFINITY;  // non-finite input: rank last, stay in range
+    z[i] = 0.f;
+    key[i] = 0;  // below every real key: never selected
+    if (e < E) {
+      z[i] = sum_splits(zpart + (static_cast<int64_t>(t) * E + e) * S, S);
+      float kv = sigmoid_f32(z[i]) + (bias ? bias[e] : 0.f);
+      if (kv != kv) kv = -INFINITY;  // non-finite input: rank last, stay in range
+      key[i] = (static_cast<uint64_t>(orderable(kv)) << 32) |
+               (0xFFFFFFFFu - static_cast<uint32_t>(e));
     }
   }
 
-  uint32_t taken = 0;
   int my_id = 0;
   float my_s = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bk = -INFINITY, bs = 0.f;
-    int bi = 0x7fffffff;
+    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < TK_MAX_SLOTS; ++i) {
-      const int e = lane + 64 * i;
-      if (i < nslots && e < E && !((taken >> i) & 1u) && ranks_before(key[i], e, bk, bi)) {
-        bk = key[i];
-        bi = e;
-        bs = sc[i];
+    for (int i = 0; i < NS; ++i)
+      if (key[i] > best) best = key[i];
+    const uint64_t win = wave_max_u64(best);
+    const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(win));
+    const int owner = id & 63, slot = id >> 6;
+    float zw = 0.f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i == slot) {
+        zw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z[i]), owner));
+        if (lane == owner) key[i] = 0;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const int oi = __shfl_xor(bi, off);
-      const float os = __shfl_xor(bs, off);
-      if (ranks_before(ok, oi, bk, bi)) {
-        bk = ok;
-        bi = oi;
-        bs = os;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == j) {
-      my_id = bi;
-      my_s = bs;
+      my_id = id;
+      my_s = sigmoid_f32(zw);
     }
   }
   // Sum of the selected scores in slot order (lane 0 .. k-1).
   float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += __shfl(my_s, j);
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
   if (lane < k) {
     const float g = renorm ? my_s / sum : my_s;
     ids[static_cast<int64_t>(t) * k + lane] = my_id;
@@ -229,25 +273,37 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpa
 hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* zpart, int T, int H,
                               int E, int S, hipStream_t stream) {
   const dim3 grid((E + RT_BN - 1) / RT_BN, (T + RT_BM - 1) / RT_BM, S);
-  router_gemm_kernel<<<grid, 256, 0, stream>>>(x, wg, zpart, T, H, E, H / S);
+  router_gemm_kernel<<<grid, 256, 0, stream>>>(x, wg, zpart, T, H, E, H / S, S);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* zpart, int S, const float* bias, int T, int E, int k,
                        float scaling, int renorm, int32_t* ids, float* w, hipStream_t stream) {
   const int blocks = (T + 3) / 4;
-  topk_kernel<<<blocks, 256, 0, stream>>>(zpart, S, bias, T, E, k, scaling, renorm, ids, w);
+  const int ns = (E + 63) / 64;
+  switch (ns) {
+#define MOE_TOPK_CASE(N) \
+  case N:                \
+    topk_kernel<N><<<blocks, 256, 0, stream>>>(zpart, S, bias, T, E, k, scaling, renorm, ids, w); \
+    break;
+    MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4) MOE_TOPK_CASE(5)
+    MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8) MOE_TOPK_CASE(9) MOE_TOPK_CASE(10)
+    MOE_TOPK_CASE(11) MOE_TOPK_CASE(12) MOE_TOPK_CASE(13) MOE_TOPK_CASE(14) MOE_TOPK_CASE(15)
+    MOE_TOPK_CASE(16)
+#undef MOE_TOPK_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 int router_split(int T, int H, int E) {
+  // Enough blocks to stream the router weight from many CUs, few enough
+  // partials that the top-k kernel reads little.
   const int tiles = ((T + RT_BM - 1) / RT_BM) * ((E + RT_BN - 1) / RT_BN);
   const int ksteps = H / RT_BK;
-  if (tiles >= 256) return 1;
-  int s = (512 + tiles - 1) / tiles;
-  if (s > 16) s = 16;
-  if (s > ksteps) s = ksteps;
-  while (s > 1 && ksteps % s) --s;
+  int s = 1;  // a power of two <= 8 that divides the k steps
+  while (s < 8 && tiles * s < 256 && ksteps % (2 * s) == 0) s *= 2;
   return s;
 }
 

@@ -130,18 +130,22 @@ def test_route_and_permute_entry_points(moe):
     assert np.array_equal(off.cpu().numpy(), o_off)
     assert np.array_equal(srt.cpu().numpy(), o_srt)
     assert np.array_equal(pos.cpu().numpy(), o_pos)
-    # permute on arbitrary (not router-made) ids, many chunks
-    rng = np.random.default_rng(7)
-    T2, E2, k2 = 5000, 40, 5
-    ids2 = np.stack([rng.choice(E2, k2, replace=False) for _ in range(T2)]).astype(np.int32)
-    ids2[:2000] = np.sort(ids2[:2000], 1)  # skewed early chunk
+
+@pytest.mark.parametrize("T2,E2,k2", [(5000, 40, 5), (70000, 300, 4), (3, 1024, 32), (1000, 7, 1)])
+def test_permute_arbitrary_ids(moe, T2, E2, k2):
+    """moe_permute on ids not made by the router: several chunks, chunks
+    ranked in several LDS passes, the largest expert count, k = 1."""
+    import torch
+    rng = np.random.default_rng(T2 + E2)
+    ids2 = np.argsort(rng.random((T2, E2)), axis=1)[:, :k2].astype(np.int32)
+    ids2[: T2 // 3] = np.sort(ids2[: T2 // 3], 1)  # a skewed stretch
     cfg2 = moe.make_config(T2, 256, E2, k2, 64, 0)
     ws2 = moe.alloc_workspace(cfg2)
     ids2_d = torch.from_numpy(ids2).cuda()
     off2 = torch.empty(E2 + 1, dtype=torch.int32, device="cuda")
     srt2 = torch.empty(T2 * k2, dtype=torch.int32, device="cuda")
     pos2 = torch.empty(T2 * k2, dtype=torch.int32, device="cuda")
-    gu.note("  moe_permute arbitrary ids")
+    gu.note(f"  moe_permute T={T2} E={E2} k={k2}")
     moe.moe_permute(cfg2, ids2_d, off2, srt2, pos2, ws2)
     torch.cuda.synchronize()
     e_off, e_srt, e_pos = oracle.permute(ids2, E2)
