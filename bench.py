@@ -50,7 +50,129 @@ def parse():
     ap.add_argument("--weight-copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES five times (to scale HBM "
+                         "traffic counters) and exit")
+    ap.add_argument("--summarize-profiles", default="", metavar="DIR",
+                    help="write profiles/*.md and profiles/traffic.json from the rocprofv3 "
+                         "outputs of PROFILE_COMMANDS under DIR, and exit (no GPU needed)")
     return ap.parse_args()
+
+
+# Commands whose outputs --summarize-profiles reads (DIR = its argument).
+PROFILE_COMMANDS = {
+    "kt_decode": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/kt_decode -o run -- "
+                 "python3 bench.py --config decode --steps 20 --warmup 5 --no-cpu --no-secondary",
+    "kt_prefill": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/kt_prefill -o run -- "
+                  "python3 bench.py --config prefill --steps 10 --warmup 3 --no-cpu --weight-copies 2",
+    "pmc_fetch_decode": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch_decode -o run -- "
+                        "python3 bench.py --config decode --steps 4 --warmup 1 --no-cpu --no-secondary",
+    "pmc_write_decode": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write_decode -o run -- "
+                        "python3 bench.py --config decode --steps 4 --warmup 1 --no-cpu --no-secondary",
+    "pmc_fetch_prefill": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch_prefill -o run -- "
+                         "python3 bench.py --config prefill --steps 2 --warmup 1 --no-cpu --weight-copies 1",
+    "pmc_write_prefill": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write_prefill -o run -- "
+                         "python3 bench.py --config prefill --steps 2 --warmup 1 --no-cpu --weight-copies 1",
+    "pmc_fetch_copy": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch_copy -o run -- "
+                      "python3 bench.py --copy-calibration 1073741824",
+    "pmc_write_copy": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write_copy -o run -- "
+                      "python3 bench.py --copy-calibration 1073741824",
+}
+KERNEL_SOURCES = {"expert_gemm": "experts.hip", "router_gemm_kernel": "router.hip",
+                  "topk_kernel": "router.hip", "combine_kernel": "experts.hip",
+                  "permute_small_kernel": "permute.hip", "rank_kernel": "permute.hip",
+                  "scan_kernel": "permute.hip", "scatter_kernel": "permute.hip"}
+
+
+def _short(name):
+    name = name.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].strip()
+
+
+def _src_sha(fname):
+    path = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", fname)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def summarize_profiles(d):
+    """Turn rocprofv3 CSV outputs under d (made by PROFILE_COMMANDS) into the
+    text summaries under profiles/ and profiles/traffic.json."""
+    import csv
+    import collections
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    for wl in ("decode", "prefill"):
+        path = os.path.join(d, f"kt_{wl}", "run_kernel_stats.csv")
+        rows = list(csv.DictReader(open(path)))
+        lines = [f"# Kernel durations, {wl} workload (rocprofv3 kernel trace)", "",
+                 "Command (from /tmp with TMPDIR=/tmp; DIR = gpurun_out of the repo):", "",
+                 "```", PROFILE_COMMANDS[f"kt_{wl}"], "```", "",
+                 "| Kernel | Calls | Average us | Min us | Max us | Share |",
+                 "|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+        lines += ["", "`__amd_rocclr_copyBuffer` is the benchmark's own weight-copy setup, outside "
+                  "the timed region.", ""]
+        with open(os.path.join(out_dir, f"kernels_{wl}.md"), "w") as f:
+            f.write("\n".join(lines))
+
+    def per_kernel(name):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(d, name, "run_counter_collection.csv"))):
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    copy_fetch = per_kernel("pmc_fetch_copy")["__amd_rocclr_copyBuffer"]
+    copy_write = per_kernel("pmc_write_copy")["__amd_rocclr_copyBuffer"]
+    cal_bytes = 1073741824
+    f_fetch = cal_bytes / (copy_fetch * 1024)   # bytes per reported KiB unit
+    f_write = cal_bytes / (copy_write * 1024)
+    traffic = {"calibration": {"copy_bytes": cal_bytes, "fetch_kib": copy_fetch,
+                               "write_kib": copy_write, "fetch_factor": f_fetch,
+                               "write_factor": f_write}}
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Each counter ran alone.  Scale: a plain 1 GiB device copy "
+             f"(`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = {copy_fetch:.0f} KiB and "
+             f"WRITE_SIZE = {copy_write:.0f} KiB, so bytes = FETCH_SIZE x 1024 x {f_fetch:.3f} "
+             f"and WRITE_SIZE x 1024 x {f_write:.3f}.", "", "Commands (from /tmp with TMPDIR=/tmp):", "", "```"]
+    lines += [PROFILE_COMMANDS[k] for k in PROFILE_COMMANDS if k.startswith("pmc_")]
+    lines += ["```", "", "| Workload | Kernel | Read MB/launch | Written MB/launch |", "|---|---|---|---|"]
+    for wl in ("decode", "prefill"):
+        fe = per_kernel(f"pmc_fetch_{wl}")
+        wr = per_kernel(f"pmc_write_{wl}")
+        for k in sorted(fe, key=lambda k: -fe[k]):
+            if "moe::" not in k:
+                continue
+            rb = fe[k] * 1024 * f_fetch
+            wb = wr.get(k, 0.0) * 1024 * f_write
+            lines.append(f"| {wl} | `{_short(k)}` | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+            short = _short(k)
+            base = short.split("<")[0]
+            key = ("gateup_kernel" if short.startswith("expert_gemm<0") else
+                   "down_kernel" if short.startswith("expert_gemm<1") else base)
+            traffic[f"{key}:{wl}"] = {"kernel": short, "read_bytes": rb, "write_bytes": wb,
+                                      "bytes_per_launch": rb + wb,
+                                      "source_sha256": _src_sha(KERNEL_SOURCES.get(base, "experts.hip"))}
+    with open(os.path.join(out_dir, "hbm_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    print(f"wrote {out_dir}")
+
+
+def copy_calibration(nbytes):
+    """Five plain device-to-device copies of nbytes: the reference for the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 5}))
 
 
 def counts(wl, U):
@@ -74,11 +196,9 @@ def traffic_for(kernel, workload):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "experts.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     ent = rec.get(f"{kernel}:{workload}")
-    if not ent or ent.get("source_sha256") != sha:
-        return None
+    if not ent or ent.get("source_sha256") != _src_sha("experts.hip"):
+        return None  # counters were taken on another version of the kernel
     return ent.get("bytes_per_launch")
 
 
@@ -188,6 +308,12 @@ def main():
               "multi-GPU path; the layer would shard by tokens or by experts, see DESIGN.md",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     import numpy as np
     import torch
 
