@@ -19,20 +19,23 @@
 //    k-contiguous in memory (weights are out x in), so A and B fragments are
 //    plain 16-byte LDS reads.
 //  * Tiles are copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR
-//    staging): one wave instruction fills 8 rows x 128 bytes; rows are
-//    gathered per lane, so the token gather of the gate/up GEMM costs
-//    nothing extra.  The 16-byte chunks of a row are XOR-swizzled by
-//    (row & 7), which keeps the fragment reads free of bank conflicts.
-//  * An S-stage ring: stage kt+S-1 is in flight while stage kt is
+//    staging): one wave instruction fills 1 KiB of LDS (8 rows of a 64-wide
+//    k step, or 16 rows of a 32-wide one); rows are gathered per lane, so
+//    the token gather of the gate/up GEMM costs nothing extra.  The 16-byte
+//    chunks of a row are XOR-swizzled so that the 64 lanes of a fragment
+//    read hit all 64 LDS banks once (no bank conflicts).
+//  * An S-stage ring: stages kt+1 .. kt+S-2 are in flight while stage kt is
 //    multiplied; per-wave `s_waitcnt vmcnt` plus a bare s_barrier order the
 //    ring (no full fence, which would drain the prefetches).
 //  * Work comes from a device-side tile list (no host synchronisation); units
 //    are spread over the 8 XCDs in contiguous ranges and walked in groups of
 //    8 row tiles so that co-resident blocks share operands in their L2.
 //
-// Two tile shapes: 256 x 256 (one block per CU, 4 waves of 128 x 128) for
-// many rows per expert, and 64 x 128 with a 3-deep ring (two blocks per CU) for few rows per
-// expert, where the GEMMs stream weights at HBM rate.
+// Two tile shapes: 256 x 256 (one block per CU, 8 waves of 128 x 64) for
+// many rows per expert, and 64 x 128 with a 3-deep ring (two blocks per CU)
+// for few rows per expert, where the GEMMs stream weights at HBM rate.
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -44,7 +47,6 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
-constexpr int BK = 64;        // k per stage: one 128-byte row segment
 constexpr int GROUP_M = 8;    // row tiles per scheduling group
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
@@ -71,24 +73,40 @@ __device__ __forceinline__ TileCoord tile_of(int u, int ntiles, int NT) {
   return {first + within % gm, within / gm};
 }
 
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int BK, int WM, int WN, int S>
 struct Cfg {
   static constexpr int NW = WM * WN;
   static constexpr int THREADS = 64 * NW;
-  static constexpr int MB = BM / WM / 32;   // 32-row blocks per wave
-  static constexpr int NB = BN / WN / 32;   // 32-col blocks per wave
-  static constexpr int JA = BM / 8 / NW;    // A DMA instructions per wave per stage
-  static constexpr int JB = BN / 8 / NW;    // B DMA instructions per wave per stage
-  static constexpr int STAGE_BYTES = (BM + BN) * 128;
+  static constexpr int MB = BM / WM / 32;     // 32-row blocks per wave
+  static constexpr int NB = BN / WN / 32;     // 32-col blocks per wave
+  static constexpr int CH = BK / 8;           // 16-byte chunks per tile row
+  static constexpr int ROWB = BK * 2;         // bytes per tile row
+  static constexpr int RPI = 64 / CH;         // rows filled by one DMA instruction
+  static constexpr int JA = BM / RPI / NW;    // A DMA instructions per wave per stage
+  static constexpr int JB = BN / RPI / NW;    // B DMA instructions per wave per stage
+  static constexpr int NI = JA + JB;
+  static constexpr int KS = BK / 16;          // MFMA k-substeps per stage
+  static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
   static constexpr int LDS_BYTES = S * STAGE_BYTES;
+  static_assert(CH == 4 || CH == 8, "k step of 32 or 64");
   static_assert(MB >= 1 && NB >= 1 && JA >= 1 && JB >= 1, "tile shape");
-  static_assert(JA + JB <= 63 / (S > 2 ? S - 2 : 1), "vmcnt budget");
+  static_assert(NI * (S > 2 ? S - 2 : 1) <= 63, "vmcnt budget");
+  // XOR swizzle of a row's 16-byte chunks.  The LDS serves 16 lanes (256
+  // bytes, 64 banks) per cycle; a fragment read has those 16 lanes on 16
+  // consecutive rows at one logical chunk.  With 128-byte rows, even and odd
+  // rows fall in different bank halves and (row >> 1) & 7 spreads the 8 rows
+  // of each half over its 8 chunk slots; with 64-byte rows, row & 3 picks the
+  // quarter and (row >> 2) & 3 the slot.  Either way the 16 lanes hit 16
+  // distinct 16-byte bank groups.
+  static __device__ __forceinline__ int swz(int row) {
+    return CH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+  }
 };
 
 // MODE 0: gate/up (+ SwiGLU), MODE 1: down (+ gating weight).
-template <int MODE, int BM, int BN, int WM, int WN, int S>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
 __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
-  using C = Cfg<BM, BN, WM, WN, S>;
+  using C = Cfg<BM, BN, BK, WM, WN, S>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int ntiles = *a.ntiles;
@@ -118,25 +136,22 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
 
-  // ---- DMA source pointers.  Instruction j of wave w fills tile rows
-  // [8 (w*J + j), +8); lane l writes row 8(w*J + j) + l/8, physical chunk
-  // l % 8, which holds logical chunk (l % 8) ^ (row & 7).
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;  // logical chunk; every DMA row r has r & 7 == lrow
-  // A rows: element offsets from the A base (x, or h), gathered per row.
+  // ---- DMA sources.  Instruction j of wave w fills tile rows
+  // [RPI (w*J + j), +RPI); lane l writes row RPI(w*J + j) + l/CH at physical
+  // chunk l % CH, which holds logical chunk (l % CH) ^ swz(row).
+  const int lrow = lane / C::CH;
+  const int pchunk = lane % C::CH;
   const uint16_t* abase;
   if (MODE == 0)
     abase = a.x;
   else
     abase = shared ? a.h_shared : a.h_routed;
-  uint32_t aoff[C::JA];
-  bool aon[C::JA];  // lanes of rows past the group's end load nothing (lane 0
-                    // re-reads row 0, so every DMA instruction is issued)
+  uint32_t aoff[C::JA];  // element offsets of the A rows (gathered by token for gate/up)
 #pragma unroll
   for (int j = 0; j < C::JA; ++j) {
-    const int r = 8 * (wid * C::JA + j) + lrow;
-    aon[j] = r < rows || lane == 0;
-    const int rr = r < rows ? r : 0;
+    const int r = C::RPI * (wid * C::JA + j) + lrow;
+    const int lchunk = pchunk ^ C::swz(r);
+    const int rr = r < rows ? r : 0;  // rows past the group's end re-read row 0 (one cached line)
     int64_t src_row;
     if (MODE == 0) {
       src_row = shared ? static_cast<int64_t>(row0 + rr) : a.sorted[row0 + rr] / a.k;
@@ -148,44 +163,47 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   }
   // B rows: each wave's rows are consecutive and lie in one matrix (for
   // gate/up the first half of the tile is W_gate, the second W_up).
-  const uint16_t* bsrc;
+  const uint16_t* bmat;
+  uint32_t boff[C::JB];  // element offsets inside that matrix
   {
-    const int r0 = 8 * wid * C::JB;  // first B row of this wave
-    const uint16_t* mat;
+    const int r0 = C::RPI * wid * C::JB;  // first B row of this wave
     int mrow;
     if (MODE == 0) {
       const bool up = r0 >= BN / 2;
-      mat = up ? (shared ? a.ws_up : a.w_up + static_cast<int64_t>(e) * a.I * H)
-               : (shared ? a.ws_gate : a.w_gate + static_cast<int64_t>(e) * a.I * H);
+      bmat = up ? (shared ? a.ws_up : a.w_up + static_cast<int64_t>(e) * a.I * H)
+                : (shared ? a.ws_gate : a.w_gate + static_cast<int64_t>(e) * a.I * H);
       mrow = n0 + r0 - (up ? BN / 2 : 0);
     } else {
-      mat = shared ? a.ws_down : a.w_down + static_cast<int64_t>(e) * H * a.I;
+      bmat = shared ? a.ws_down : a.w_down + static_cast<int64_t>(e) * H * a.I;
       mrow = n0 + r0;
     }
-    bsrc = mat + static_cast<int64_t>(mrow + lrow) * K + lchunk * 8;
+#pragma unroll
+    for (int j = 0; j < C::JB; ++j) {
+      const int lchunk = pchunk ^ C::swz(r0 + C::RPI * j + lrow);
+      boff[j] = static_cast<uint32_t>((mrow + C::RPI * j + lrow) * K + lchunk * 8);
+    }
   }
 
-  auto issue = [&](int kt) {
+  // DMA instruction d (0 <= d < NI) of stage kt: A rows first, then B rows.
+  auto issue_one = [&](int kt, int d) {
     uint8_t* st = smem + (kt % S) * C::STAGE_BYTES;
     const int k0 = kt * BK;
-#pragma unroll
-    for (int j = 0; j < C::JA; ++j)
-      if (aon[j]) dma16(abase + aoff[j] + k0, st + (wid * C::JA + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < C::JB; ++j)
-      dma16(bsrc + static_cast<int64_t>(8 * j) * K + k0,
-            st + BM * 128 + (wid * C::JB + j) * 1024);
+    if (d < C::JA) {
+      dma16(abase + aoff[d] + k0, st + (wid * C::JA + d) * 1024);
+    } else {
+      const int j = d - C::JA;
+      dma16(bmat + boff[j] + k0, st + BM * C::ROWB + (wid * C::JB + j) * 1024);
+    }
   };
 
   // ---- fragment addressing.  Wave (wm, wn) owns rows [wm*BM/WM, +BM/WM).
   const int wm = wid / WN, wn = wid % WN;
   const int fr = lane & 31;
   const int fh = lane >> 5;
-  // Byte offset of (row, logical chunk c) inside a stage: row*128 + ((c ^ (row&7)) * 16);
-  // fr & 7 == row & 7 for every fragment row since blocks start at multiples of 32.
+  const int fswz = C::swz(fr);  // fragment rows start at multiples of 32
   int a_off[C::MB];
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) a_off[mb] = (wm * (BM / WM) + 32 * mb + fr) * 128;
+  for (int mb = 0; mb < C::MB; ++mb) a_off[mb] = (wm * (BM / WM) + 32 * mb + fr) * C::ROWB;
   int b_off[C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
@@ -198,30 +216,11 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     } else {
       brow = wn * (BN / WN) + 32 * nb;
     }
-    b_off[nb] = BM * 128 + (brow + fr) * 128;
+    b_off[nb] = BM * C::ROWB + (brow + fr) * C::ROWB;
   }
+
   const int KT = K / BK;
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < KT) issue(s);
-
-  // The ring protocol, shared by waves that multiply and waves whose rows
-  // all lie past the group's end (those only keep the barriers and DMAs).
-  auto ring_step = [&](int kt) {
-    if (kt + S - 2 < KT)
-      wait_vmcnt<(S - 2) * (C::JA + C::JB)>();
-    else
-      wait_vmcnt<0>();
-    // Bare barrier: orders the ring without draining the prefetches (the
-    // "memory" clobber keeps the compiler from moving LDS accesses across).
-    asm volatile("s_barrier" ::: "memory");
-    if (kt + S - 1 < KT) issue(kt + S - 1);
-  };
-
-  if (wm * (BM / WM) >= rows) {
-    for (int kt = 0; kt < KT; ++kt) ring_step(kt);
-    return;
-  }
+  const bool has_rows = wm * (BM / WM) < rows;  // else: keep the ring going only
 
   f32x16 acc[C::MB][C::NB];
 #pragma unroll
@@ -229,33 +228,170 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f32x16{};
 
-  for (int kt = 0; kt < KT; ++kt) {
-    ring_step(kt);
-    // Fragments of k-substep ks+1 are read while the MFMAs of ks run; the
-    // scheduling barriers keep at most two fragment sets live.
+  bf16x8 af[2][C::MB], bf[2][C::NB];
+  auto load_frags = [&](int kt, int ks, int set) {
     const uint8_t* st = smem + (kt % S) * C::STAGE_BYTES;
-    bf16x8 af[2][C::MB], bf[2][C::NB];
-    auto load_frags = [&](int ks, int set) {
-      const int sw = ((2 * ks + fh) ^ (fr & 7)) * 16;
+    const int sw = ((2 * ks + fh) ^ fswz) * 16;
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-        bf[set][nb] = *reinterpret_cast<const bf16x8*>(st + b_off[nb] + sw);
+    for (int nb = 0; nb < C::NB; ++nb)
+      bf[set][nb] = *reinterpret_cast<const bf16x8*>(st + b_off[nb] + sw);
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-        af[set][mb] = *reinterpret_cast<const bf16x8*>(st + a_off[mb] + sw);
-    };
-    load_frags(0, 0);
+    for (int mb = 0; mb < C::MB; ++mb)
+      af[set][mb] = *reinterpret_cast<const bf16x8*>(st + a_off[mb] + sw);
+  };
+  // The MFMAs of one k-substep; `dma(i)` may issue a refill DMA after MFMA i.
+  auto mfmas = [&](int set, auto dma) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) load_frags(ks + 1, (ks + 1) & 1);
+    for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
+      for (int nb = 0; nb < C::NB; ++nb) {
+        acc[mb][nb] = mfma32(af[set][mb], bf[set][nb], acc[mb][nb]);
+        dma(mb * C::NB + nb);
+      }
+  };
+  // A bare barrier orders the ring without draining in-flight prefetches
+  // (a full fence would); the "memory" clobber keeps LDS accesses in place.
+  auto barrier = [] { asm volatile("s_barrier" ::: "memory"); };
+
+  if constexpr (S >= 4) {
+    // Ring of S >= 4 buffers, two stages in flight.  Step kt: refill stage
+    // kt+2 (buffer of stage kt-2) during the first half of stage kt's MFMAs;
+    // mid-stage, wait for stage kt+1 and pass the barrier that publishes it;
+    // then read stage kt+1's first fragments while the second half of stage
+    // kt's MFMAs runs.  The barrier passed mid-stage kt-1 guarantees every
+    // wave is done with stage kt-2 before its refill.  Within a k-substep the
+    // next fragments are requested after the substep's first MFMA, so the
+    // wait before that MFMA only covers reads a whole substep old.
+    constexpr int HALF = C::KS / 2;
+    constexpr int PER_SUB = C::MB * C::NB;
+    constexpr int DMA_EVERY = (HALF * PER_SUB) / C::NI > 0 ? (HALF * PER_SUB) / C::NI : 1;
+    constexpr int DMA_IN_MFMA = (HALF * PER_SUB) / DMA_EVERY < C::NI ? (HALF * PER_SUB) / DMA_EVERY
+                                                                       : C::NI;
+    static_assert(C::KS % 2 == 0, "two halves per stage");
+    for (int s = 0; s < 2; ++s)
+      if (s < KT)
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-          acc[mb][nb] = mfma32(af[ks & 1][mb], bf[ks & 1][nb], acc[mb][nb]);
+        for (int d = 0; d < C::NI; ++d) issue_one(s, d);
+    if (KT > 1)
+      wait_vmcnt<C::NI>();
+    else
+      wait_vmcnt<0>();
+    barrier();
+
+    // One k-substep: first MFMA, then the next fragment reads, then the rest
+    // of the MFMAs (with refill DMAs after MFMA i when dma(i) says so).
+    auto substep = [&](int set, auto next_reads, auto dma) {
+      acc[0][0] = mfma32(af[set][0], bf[set][0], acc[0][0]);
+      dma(0);
       __builtin_amdgcn_sched_barrier(0);
+      next_reads();
+#pragma unroll
+      for (int i = 1; i < PER_SUB; ++i) {
+        const int mb = i / C::NB, nb = i % C::NB;
+        acc[mb][nb] = mfma32(af[set][mb], bf[set][nb], acc[mb][nb]);
+        dma(i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // REFILL: stage kt+2 exists; LAST: kt is the final stage.
+    auto step = [&](int kt, auto REFILL, auto LAST) {
+      constexpr bool refill = decltype(REFILL)::value, last = decltype(LAST)::value;
+#pragma unroll
+      for (int ks = 0; ks < HALF; ++ks) {
+        substep(
+            ks & 1, [&] { load_frags(kt, ks + 1, (ks + 1) & 1); },
+            [&](int i) {
+              const int g = ks * PER_SUB + i;  // MFMA index in this half
+              if (refill && g % DMA_EVERY == DMA_EVERY - 1 && g / DMA_EVERY < DMA_IN_MFMA)
+                issue_one(kt + 2, g / DMA_EVERY);
+            });
+      }
+      if (refill)
+#pragma unroll
+        for (int d = DMA_IN_MFMA; d < C::NI; ++d) issue_one(kt + 2, d);
+      if (!last) {
+        if (refill)
+          wait_vmcnt<C::NI>();
+        else
+          wait_vmcnt<0>();
+        barrier();
+      }
+#pragma unroll
+      for (int ks = HALF; ks < C::KS; ++ks) {
+        substep(
+            ks & 1,
+            [&] {
+              if (ks + 1 < C::KS)
+                load_frags(kt, ks + 1, (ks + 1) & 1);
+              else if (!last)
+                load_frags(kt + 1, 0, 0);
+            },
+            [](int) {});
+      }
+    };
+    // Waves without rows keep the same DMA and barrier sequence.
+    auto ring_only = [&](int kt, bool refill, bool last) {
+      if (refill)
+        for (int d = 0; d < C::NI; ++d) issue_one(kt + 2, d);
+      if (!last) {
+        if (refill)
+          wait_vmcnt<C::NI>();
+        else
+          wait_vmcnt<0>();
+        barrier();
+      }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (has_rows) {
+      load_frags(0, 0, 0);
+      for (int kt = 0; kt + 2 < KT; ++kt) step(kt, T_{}, F_{});
+      if (KT >= 2) step(KT - 2, F_{}, F_{});
+      step(KT - 1, F_{}, T_{});
+    } else {
+      for (int kt = 0; kt < KT; ++kt) ring_only(kt, kt + 2 < KT, kt + 1 == KT);
+    }
+  } else {
+    // Ring of S buffers, S-1 stages in flight: wait for stage kt, barrier
+    // (all waves' DMAs of stage kt landed, all waves done with stage kt-1,
+    // whose buffer stage kt+S-1 refills), then the stage's MFMAs with the
+    // refill DMAs spread between them.
+    constexpr int MFMAS = C::KS * C::MB * C::NB;
+    constexpr int DMA_EVERY = MFMAS / C::NI > 0 ? MFMAS / C::NI : 1;
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < KT)
+#pragma unroll
+        for (int d = 0; d < C::NI; ++d) issue_one(s, d);
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + S - 2 < KT)
+        wait_vmcnt<(S - 2) * C::NI>();
+      else
+        wait_vmcnt<0>();
+      barrier();
+      const bool refill = kt + S - 1 < KT;
+      if (!has_rows) {
+        if (refill)
+          for (int d = 0; d < C::NI; ++d) issue_one(kt + S - 1, d);
+        continue;
+      }
+      load_frags(kt, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + 1 < C::KS) load_frags(kt, ks + 1, (ks + 1) & 1);
+        mfmas(ks & 1, [&](int i) {
+          const int g = ks * C::MB * C::NB + i;  // MFMA index in the stage
+          if (g % DMA_EVERY == DMA_EVERY - 1 && g / DMA_EVERY < C::NI && refill)
+            issue_one(kt + S - 1, g / DMA_EVERY);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (refill && MFMAS / DMA_EVERY < C::NI)  // more DMAs than MFMA slots
+#pragma unroll
+        for (int d = MFMAS / DMA_EVERY; d < C::NI; ++d) issue_one(kt + S - 1, d);
     }
   }
+  if (!has_rows) return;
 
   // ---- epilogue
   if (MODE == 0) {
@@ -336,19 +472,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   *reinterpret_cast<u32x4*>(y + t * H + d) = outv;
 }
 
-// Tile shapes.
-using BigTile = Cfg<256, 256, 2, 2, 2>;
-using SmallTile = Cfg<64, 128, 2, 2, 3>;
-
-template <int MODE, int BM, int BN, int WM, int WN, int S>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
 hipError_t launch_one(const ExpertArgs& a, int tile_capacity, int NT, hipStream_t stream) {
-  using C = Cfg<BM, BN, WM, WN, S>;
+  using C = Cfg<BM, BN, BK, WM, WN, S>;
   const int64_t units = static_cast<int64_t>(tile_capacity) * NT;
   const int64_t grid = (units + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid <= 0) return hipSuccess;
   ExpertArgs b = a;
   b.NT = NT;
-  expert_gemm<MODE, BM, BN, WM, WN, S><<<static_cast<unsigned>(grid), C::THREADS, 0, stream>>>(b);
+  expert_gemm<MODE, BM, BN, BK, WM, WN, S>
+      <<<static_cast<unsigned>(grid), C::THREADS, 0, stream>>>(b);
   return hipGetLastError();
 }
 
@@ -372,19 +505,21 @@ int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape) {
   return static_cast<int>(routed + sh);
 }
 
+// Tile shapes: big = 256 x 256, k step 32, 4-deep ring with two stages in
+// flight, 8 waves of 128 x 64 (two per SIMD, so one wave's stalls are
+// covered by the other's MFMAs); small = 64 x 128, k step 64, 3-deep ring,
+// 4 waves, two blocks per CU.
 hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream) {
   const int maxn = std::max(a.I, a.Is);
-  if (shape == kTileBig) {
-    return launch_one<0, 256, 256, 2, 2, 2>(a, tile_capacity, (maxn + 127) / 128, stream);
-  }
-  return launch_one<0, 64, 128, 2, 2, 3>(a, tile_capacity, (maxn + 63) / 64, stream);
+  if (shape == kTileBig)
+    return launch_one<0, 256, 256, 32, 2, 4, 4>(a, tile_capacity, (maxn + 127) / 128, stream);
+  return launch_one<0, 64, 128, 64, 2, 2, 3>(a, tile_capacity, (maxn + 63) / 64, stream);
 }
 
 hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream) {
-  if (shape == kTileBig) {
-    return launch_one<1, 256, 256, 2, 2, 2>(a, tile_capacity, a.H / 256, stream);
-  }
-  return launch_one<1, 64, 128, 2, 2, 3>(a, tile_capacity, a.H / 128, stream);
+  if (shape == kTileBig)
+    return launch_one<1, 256, 256, 32, 2, 4, 4>(a, tile_capacity, a.H / 256, stream);
+  return launch_one<1, 64, 128, 64, 2, 2, 3>(a, tile_capacity, a.H / 128, stream);
 }
 
 hipError_t launch_combine(const uint16_t* o_routed, const uint16_t* o_shared,
