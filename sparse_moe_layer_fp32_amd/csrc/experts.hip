@@ -245,7 +245,7 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
-        acc[mb][nb] = mfma32(af[set][mb], bf[set][nb], acc[mb][nb]);
+        acc[mb][nb] = mfma32(bf[set][nb], af[set][mb], acc[mb][nb]);
         dma(mb * C::NB + nb);
       }
   };
@@ -281,14 +281,14 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     // One k-substep: first MFMA, then the next fragment reads, then the rest
     // of the MFMAs (with refill DMAs after MFMA i when dma(i) says so).
     auto substep = [&](int set, auto next_reads, auto dma) {
-      acc[0][0] = mfma32(af[set][0], bf[set][0], acc[0][0]);
+      acc[0][0] = mfma32(bf[set][0], af[set][0], acc[0][0]);
       dma(0);
       __builtin_amdgcn_sched_barrier(0);
       next_reads();
 #pragma unroll
       for (int i = 1; i < PER_SUB; ++i) {
         const int mb = i / C::NB, nb = i % C::NB;
-        acc[mb][nb] = mfma32(af[set][mb], bf[set][nb], acc[mb][nb]);
+        acc[mb][nb] = mfma32(bf[set][nb], af[set][mb], acc[mb][nb]);
         dma(i);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -393,42 +393,50 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   }
   if (!has_rows) return;
 
-  // ---- epilogue
+  // ---- epilogue.  The MFMAs take the weight rows as their first operand,
+  // so acc[mb][nb] holds the transposed block: lane l owns token row
+  // 32 mb + (l % 32) of the wave's rows and, for r = 4g .. 4g+3, the four
+  // consecutive output columns 8g + 4(l / 32) + 0..3 of block nb.  Each
+  // group of four goes out as one 8-byte store.
+  const int row = wm * (BM / WM) + fr;  // + 32 mb
   if (MODE == 0) {
     uint16_t* out = shared ? a.h_shared : a.h_routed;
     const float lim = shared ? a.limit_shared : a.limit;
     const int half = C::NB / 2;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
+      if (row + 32 * mb >= rows) continue;
+      uint16_t* orow = out + static_cast<int64_t>(row0 + row + 32 * mb) * N + n0 +
+                       wn * (BN / 2 / WN) + 4 * fh;
 #pragma unroll
-      for (int nb = 0; nb < half; ++nb) {
-        const int col = n0 + wn * (BN / 2 / WN) + 32 * nb + fr;
+      for (int nb = 0; nb < half; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * (BM / WM) + 32 * mb + mfma32_row(r, lane);
-          if (row < rows) {
-            const float hv = swiglu_f32(acc[mb][nb][r], acc[mb][nb + half][r], lim);
-            out[static_cast<int64_t>(row0 + row) * N + col] =
-                static_cast<uint16_t>(f32_to_bf16_bits(hv));
-          }
+        for (int g = 0; g < 4; ++g) {
+          float hv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            hv[q] = swiglu_f32(acc[mb][nb][4 * g + q], acc[mb][nb + half][4 * g + q], lim);
+          *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * g) =
+              make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
-      }
     }
   } else {
     uint16_t* out = shared ? a.o_shared : a.o_routed;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
+      if (row + 32 * mb >= rows) continue;
+      const float wt = shared ? 1.0f : a.topk_w[a.sorted[row0 + row + 32 * mb]];
+      uint16_t* orow =
+          out + static_cast<int64_t>(row0 + row + 32 * mb) * H + n0 + wn * (BN / WN) + 4 * fh;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * (BM / WM) + 32 * mb + mfma32_row(r, lane);
-        if (row < rows) {
-          const float wt = shared ? 1.0f : a.topk_w[a.sorted[row0 + row]];
-          uint16_t* orow = out + static_cast<int64_t>(row0 + row) * H + n0 + wn * (BN / WN) + fr;
+      for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-            orow[32 * nb] = static_cast<uint16_t>(f32_to_bf16_bits(acc[mb][nb][r] * wt));
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& v = acc[mb][nb];
+          *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * g) =
+              make_uint2(pack_bf16x2(v[4 * g] * wt, v[4 * g + 1] * wt),
+                         pack_bf16x2(v[4 * g + 2] * wt, v[4 * g + 3] * wt));
         }
-      }
     }
   }
 }
@@ -457,14 +465,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
   }
-  for (int j = 0; j < k; ++j) {
-    const int64_t pos = min(max(pair_pos[t * k + j], 0), P - 1);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(o_routed + pos * H + d);
+  // Slots in chunks of 8: all positions, then all rows, are requested
+  // before the first add, so the loads overlap; the adds stay in slot order.
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int64_t pos[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += bf16_lo(v[q]);
-      acc[2 * q + 1] += bf16_hi(v[q]);
-    }
+    for (int j = 0; j < 8; ++j)
+      pos[j] = j0 + j < k ? min(max(pair_pos[t * k + j0 + j], 0), P - 1) : -1;
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (pos[j] >= 0) v[j] = *reinterpret_cast<const u32x4*>(o_routed + pos[j] * H + d);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (pos[j] >= 0)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += bf16_lo(v[j][q]);
+          acc[2 * q + 1] += bf16_hi(v[j][q]);
+        }
   }
   u32x4 outv;
 #pragma unroll

@@ -35,7 +35,7 @@ __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uin
 }
 
 // zpart[t][e][s] = sum over k in split s of x[t][k] * wg[e][k] (the split
-// partials of one logit are contiguous, S in {1, 2, 4, 8}).
+// partials of one logit are contiguous, S a power of two <= 32).
 // Grid: (ceil(E/64), ceil(T/64), S); 256 threads = 4 waves in a 2x2 layout,
 // each wave one 32x32 output block.
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
@@ -193,19 +193,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return a > b ? a : b;
 }
 
-// Sum of the S split partials of one logit, in split order.
+// Sum of the S split partials of one logit, in split order (S a power of
+// two <= 32; the partials of one logit are contiguous).
 __device__ __forceinline__ float sum_splits(const float* p, int S) {
   if (S == 1) return p[0];
   if (S == 2) {
     const float2 a = *reinterpret_cast<const float2*>(p);
     return a.x + a.y;
   }
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  float acc = ((a[0] + a[1]) + a[2]) + a[3];
-  if (S == 8) {
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-    acc = (((acc + b[0]) + b[1]) + b[2]) + b[3];
-  }
+  f32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (4 * i < S) v[i] = *reinterpret_cast<const f32x4*>(p + 4 * i);
+  float acc = v[0][0];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (4 * i < S)
+#pragma unroll
+      for (int q = (i == 0 ? 1 : 0); q < 4; ++q) acc += v[i][q];
   return acc;
 }
 
@@ -298,12 +303,13 @@ hipError_t launch_topk(const float* zpart, int S, const float* bias, int T, int 
 }
 
 int router_split(int T, int H, int E) {
-  // Enough blocks to stream the router weight from many CUs, few enough
-  // partials that the top-k kernel reads little.
+  // Enough blocks to stream the router weight from many CUs (a few tiles,
+  // as in decoding, split k up to 32 ways), few enough partials that the
+  // top-k kernel reads little.
   const int tiles = ((T + RT_BM - 1) / RT_BM) * ((E + RT_BN - 1) / RT_BN);
   const int ksteps = H / RT_BK;
-  int s = 1;  // a power of two <= 8 that divides the k steps
-  while (s < 8 && tiles * s < 256 && ksteps % (2 * s) == 0) s *= 2;
+  int s = 1;  // a power of two <= 32 that divides the k steps
+  while (s < 32 && tiles * s < 256 && ksteps % (2 * s) == 0) s *= 2;
   return s;
 }
 
