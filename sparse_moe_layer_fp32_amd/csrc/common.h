@@ -38,12 +38,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float sigmoid_f32(float v) { return 1.0f / (1.0f + expf(-v)); }
 
 // SiLU(g) * u with the optional clamp: g <= L, -L <= u <= L when L > 0.
+// SiLU(g) = g / (1 + e^-g) with e^-g = 2^(-g log2 e) from v_exp_f32 and the
+// reciprocal from v_rcp_f32 (each about 1 ulp): the result is rounded to
+// bf16 right after, so the approximation is far below that rounding.
+// Large negative g: 2^(large) = inf, 1/inf = 0, SiLU -> -0.
 __device__ __forceinline__ float swiglu_f32(float g, float u, float limit) {
   if (limit > 0.0f) {
     g = fminf(g, limit);
     u = fminf(fmaxf(u, -limit), limit);
   }
-  return g / (1.0f + expf(-g)) * u;
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // ------------------------------------------------------------------ MFMA
@@ -54,23 +59,21 @@ __device__ __forceinline__ float swiglu_f32(float g, float u, float limit) {
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ int mfma32_row(int r, int lane) {
-  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-
 // ---------------------------------------------------------- XCD mapping
 // Blocks are dispatched to XCDs round-robin (block b -> XCD b % 8).  Given
-// `nvalid` units of work spread over `gridsize` blocks, give each XCD a
-// contiguous range of units so that blocks sharing operands share an L2.
-// Returns -1 for a block without work.
-__device__ __forceinline__ int xcd_remap(int bid, int gridsize, int nvalid) {
+// `nvalid` units of work, give each XCD a contiguous range of units so that
+// blocks sharing operands share an L2.  Returns -1 for a block without work.
+__device__ __forceinline__ int xcd_remap(int bid, int nvalid) {
   const int per = (nvalid + kNumXcd - 1) / kNumXcd;
   const int xcd = bid % kNumXcd;
   const int slot = bid / kNumXcd;
   if (slot >= per) return -1;
   const int u = xcd * per + slot;
-  (void)gridsize;
   return u < nvalid ? u : -1;
+}
+
+__device__ __forceinline__ int mfma32_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
 }  // namespace moe

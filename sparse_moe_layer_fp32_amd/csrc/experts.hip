@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int ntiles = *a.ntiles;
-  const int u = xcd_remap(blockIdx.x, gridDim.x, ntiles * a.NT);
+  const int u = xcd_remap(blockIdx.x, ntiles * a.NT);
   if (u < 0) return;
   const TileCoord tc = tile_of(u, ntiles, a.NT);
   const int2 tile = a.tiles[tc.mt];
@@ -221,6 +221,14 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
 
   const int KT = K / BK;
   const bool has_rows = wm * (BM / WM) < rows;  // else: keep the ring going only
+  // Down: gating weight of each of this lane's output rows, requested now,
+  // used in the epilogue.
+  float wt[C::MB];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int r = wm * (BM / WM) + 32 * mb + fr;
+    wt[mb] = (MODE == 1 && !shared && r < rows) ? a.w_sorted[row0 + r] : 1.0f;
+  }
 
   f32x16 acc[C::MB][C::NB];
 #pragma unroll
@@ -425,7 +433,6 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
       if (row + 32 * mb >= rows) continue;
-      const float wt = shared ? 1.0f : a.topk_w[a.sorted[row0 + row + 32 * mb]];
       uint16_t* orow =
           out + static_cast<int64_t>(row0 + row + 32 * mb) * H + n0 + wn * (BN / WN) + 4 * fh;
 #pragma unroll
@@ -434,8 +441,8 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
         for (int g = 0; g < 4; ++g) {
           const f32x16& v = acc[mb][nb];
           *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * g) =
-              make_uint2(pack_bf16x2(v[4 * g] * wt, v[4 * g + 1] * wt),
-                         pack_bf16x2(v[4 * g + 2] * wt, v[4 * g + 3] * wt));
+              make_uint2(pack_bf16x2(v[4 * g] * wt[mb], v[4 * g + 1] * wt[mb]),
+                         pack_bf16x2(v[4 * g + 2] * wt[mb], v[4 * g + 3] * wt[mb]));
         }
     }
   }

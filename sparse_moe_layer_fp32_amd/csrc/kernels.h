@@ -10,12 +10,13 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
+constexpr int kTopkBlockTokens = 2048;  // below: one top-k block per token
 
 // Arguments of the grouped expert GEMMs (gate/up and down share them).
 struct ExpertArgs {
   const uint16_t* x;        // [T][H]
   const int32_t* sorted;    // [P] pair ids in expert order
-  const float* topk_w;      // [T][k] gating weights (pair order)
+  const float* w_sorted;    // [P] gating weights in expert order (w_sorted[i] = w[sorted[i]])
   int k;
   int64_t T;
   int H, I, Is, E;
@@ -50,7 +51,8 @@ hipError_t launch_topk(const float* zpart, int S, const float* bias, int T, int 
 hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, int with_shared,
                           int32_t* rank, int32_t* hist, int32_t* base, int32_t* offsets,
                           int32_t* sorted, int32_t* pos, int2* tiles, int32_t* ntiles,
-                          hipStream_t stream, hipEvent_t* ev);
+                          const float* topk_w, float* w_sorted, hipStream_t stream,
+                          hipEvent_t* ev);
 
 hipError_t launch_fill_zero(int32_t* p, int n, hipStream_t stream);
 int permute_chunk(int P);        // pairs per rank/histogram chunk (at most 64 chunks)

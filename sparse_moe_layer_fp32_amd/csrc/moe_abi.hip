@@ -39,7 +39,7 @@ struct Plan {
   int C;         // permutation chunks, padded to a multiple of 4
   int shape;     // expert GEMM tile shape (kTileBig / kTileSmall)
   int tile_cap;  // capacity of the GEMM tile list
-  size_t zpart, ids, w, rank, hist, base, offsets, sorted, pos, tiles, ntiles, h, o, total;
+  size_t zpart, ids, w, rank, hist, base, offsets, sorted, pos, wsorted, tiles, ntiles, h, o, total;
 };
 
 moe_status validate(const moe_config* c) {
@@ -97,6 +97,7 @@ void make_plan(const moe_config* c, Plan* p) {
   p->offsets = take((static_cast<size_t>(p->E) + 1) * 4);
   p->sorted = take(P * 4);
   p->pos = take(P * 4);
+  p->wsorted = take(P * 4);
   p->tiles = take(static_cast<size_t>(p->tile_cap) * 8);
   p->ntiles = take(16);
   p->h = take((P * p->I + T64 * p->Is) * 2);
@@ -143,13 +144,17 @@ moe_status route_impl(const Plan& p, const moe_config* c, const uint16_t* x, con
   return MOE_OK;
 }
 
+// w (may be NULL): gating weights in pair order, gathered into expert order
+// in the workspace for the down GEMM's epilogue.
 moe_status permute_impl(const Plan& p, const int32_t* ids, int32_t* offsets, int32_t* sorted,
-                        int32_t* pos, void* ws, hipStream_t stream, hipEvent_t* ev) {
+                        int32_t* pos, const float* w, void* ws, hipStream_t stream,
+                        hipEvent_t* ev) {
   MOE_CHECK_LAUNCH(
       moe::launch_permute(ids, static_cast<int>(p.P), p.E, p.T, moe::experts_tile_rows(p.shape),
                           p.Is > 0, at<int32_t>(ws, p.rank), at<int32_t>(ws, p.hist),
                           at<int32_t>(ws, p.base), offsets, sorted, pos, at<int2>(ws, p.tiles),
-                          at<int32_t>(ws, p.ntiles), stream, ev),
+                          at<int32_t>(ws, p.ntiles), w, w ? at<float>(ws, p.wsorted) : nullptr,
+                          stream, ev),
       "permute");
   return MOE_OK;
 }
@@ -186,13 +191,13 @@ moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* rou
   uint16_t* o_shared = p.Is > 0 ? o_routed + static_cast<size_t>(p.P) * p.H : nullptr;
 
   if ((st = route_impl(p, c, x, router_w, router_bias, ids, w, ws, stream, ev))) return st;
-  if ((st = permute_impl(p, ids, offsets, sorted, pos, ws, stream, ev ? ev + 2 : nullptr)))
+  if ((st = permute_impl(p, ids, offsets, sorted, pos, w, ws, stream, ev ? ev + 2 : nullptr)))
     return st;
 
   moe::ExpertArgs g{};
   g.x = x;
   g.sorted = sorted;
-  g.topk_w = w;
+  g.w_sorted = at<float>(ws, p.wsorted);
   g.k = p.k;
   g.T = p.T;
   g.H = p.H;
@@ -276,7 +281,8 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
     MOE_CHECK_LAUNCH(moe::launch_fill_zero(expert_offsets, p.E + 1, stream), "zero offsets");
     return ok();
   }
-  if ((st = permute_impl(p, topk_ids, expert_offsets, sorted_pairs, pair_pos, ws, stream, nullptr)))
+  if ((st = permute_impl(p, topk_ids, expert_offsets, sorted_pairs, pair_pos, nullptr, ws, stream,
+                         nullptr)))
     return st;
   return ok();
 }

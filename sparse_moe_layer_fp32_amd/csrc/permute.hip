@@ -164,7 +164,8 @@ __device__ void block_rank(const int32_t* sid, int n, int E, int nbits,
 __global__ __launch_bounds__(1024) void permute_small_kernel(
     const int32_t* __restrict__ ids, int P, int E, int64_t T, int bm, int with_shared,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
-    int2* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+    int2* __restrict__ tiles, int32_t* __restrict__ ntiles, const float* __restrict__ topk_w,
+    float* __restrict__ w_sorted) {
   __shared__ int32_t sid[kSmallPairs];
   __shared__ int32_t srank[kSmallPairs];
   __shared__ int32_t wcnt[16][kMaxExperts];
@@ -185,6 +186,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     const int i = run[e] + srank[p];
     sorted[i] = p;
     pos[p] = i;
+    if (w_sorted) w_sorted[i] = topk_w[p];
   }
 }
 
@@ -271,7 +273,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
                                                       const int32_t* __restrict__ offsets, int P,
                                                       int E, int Cp, int chunk,
                                                       int32_t* __restrict__ sorted,
-                                                      int32_t* __restrict__ pos) {
+                                                      int32_t* __restrict__ pos,
+                                                      const float* __restrict__ topk_w,
+                                                      float* __restrict__ w_sorted) {
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= P) return;
   const int e = ids[p];
@@ -280,6 +284,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int i = offsets[e] + base[static_cast<int64_t>(e) * Cp + c] + rank[p];
   sorted[i] = p;
   pos[p] = i;
+  if (w_sorted) w_sorted[i] = topk_w[p];
 }
 
 __global__ void fill_zero_kernel(int32_t* __restrict__ p, int n) {
@@ -310,11 +315,12 @@ hipError_t launch_fill_zero(int32_t* p, int n, hipStream_t stream) {
 hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, int with_shared,
                           int32_t* rank, int32_t* hist, int32_t* base, int32_t* offsets,
                           int32_t* sorted, int32_t* pos, int2* tiles, int32_t* ntiles,
-                          hipStream_t stream, hipEvent_t* ev) {
+                          const float* topk_w, float* w_sorted, hipStream_t stream,
+                          hipEvent_t* ev) {
   if (P <= kSmallPairs) {
     if (ev) hipEventRecord(ev[0], stream);
     permute_small_kernel<<<1, 1024, 0, stream>>>(ids, P, E, T, bm, with_shared, offsets, sorted,
-                                                 pos, tiles, ntiles);
+                                                 pos, tiles, ntiles, topk_w, w_sorted);
     if (ev) {
       hipEventRecord(ev[1], stream);
       hipEventRecord(ev[2], stream);
@@ -335,7 +341,7 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, i
   if (err != hipSuccess) return err;
   if (ev) hipEventRecord(ev[2], stream);
   scatter_kernel<<<(P + 255) / 256, 256, 0, stream>>>(ids, rank, base, offsets, P, E, Cp, chunk,
-                                                      sorted, pos);
+                                                      sorted, pos, topk_w, w_sorted);
   return hipGetLastError();
 }
 

@@ -273,6 +273,103 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpa
   }
 }
 
+// Few tokens, many partials: one 256-thread block per token, thread i
+// holding experts i, i + 256, ...  Each wave selects its own top k (as
+// above); wave 0 then selects the top k of the 4k candidates.  Every expert
+// of the global top k is in its wave's top k, and the keys and scores are
+// those of topk_kernel, so the two kernels give identical results.
+template <int NS>
+__global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict__ zpart, int S,
+                                                         const float* __restrict__ bias, int T,
+                                                         int E, int k, float scaling, int renorm,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ w) {
+  __shared__ uint64_t cand_key[4][kMaxTopK];
+  __shared__ float cand_z[4][kMaxTopK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = blockIdx.x;
+
+  float z[NS];
+  uint64_t key[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int e = tid + 256 * i;
+    z[i] = 0.f;
+    key[i] = 0;
+    if (e < E) {
+      z[i] = sum_splits(zpart + (static_cast<int64_t>(t) * E + e) * S, S);
+      float kv = sigmoid_f32(z[i]) + (bias ? bias[e] : 0.f);
+      if (kv != kv) kv = -INFINITY;
+      key[i] = (static_cast<uint64_t>(orderable(kv)) << 32) |
+               (0xFFFFFFFFu - static_cast<uint32_t>(e));
+    }
+  }
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (key[i] > best) best = key[i];
+    const uint64_t win = wave_max_u64(best);
+    float zw = 0.f;
+    if (win != 0) {  // 0: this wave has no keys left
+      const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(win));
+      const int owner = id & 63, slot = id >> 8;
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        if (i == slot) {
+          zw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z[i]), owner));
+          if (lane == owner) key[i] = 0;
+        }
+    }
+    if (lane == 0) {
+      cand_key[wave][j] = win;
+      cand_z[wave][j] = zw;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  // Lane l holds candidates l and l + 64 of the 4k (wave-major order).
+  uint64_t ck[2];
+  float cz[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = lane + 64 * h;
+    ck[h] = 0;
+    cz[h] = 0.f;
+    if (c < 4 * k) {
+      ck[h] = cand_key[c / k][c % k];
+      cz[h] = cand_z[c / k][c % k];
+    }
+  }
+  int my_id = 0;
+  float my_s = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const uint64_t best = ck[0] > ck[1] ? ck[0] : ck[1];
+    const uint64_t win = wave_max_u64(best);
+    const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(win));
+    // The holder of the winning key publishes its logit.
+    const int h = ck[1] == win ? 1 : 0;
+    const bool mine = ck[h] == win;
+    const uint64_t mask = __ballot(mine);
+    const int holder = __builtin_ctzll(mask);
+    const float zsel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h ? cz[1] : cz[0]), holder));
+    if (mine) ck[h] = 0;
+    if (lane == j) {
+      my_id = id;
+      my_s = sigmoid_f32(zsel);
+    }
+  }
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
+  if (lane < k) {
+    const float g = renorm ? my_s / sum : my_s;
+    ids[static_cast<int64_t>(t) * k + lane] = my_id;
+    w[static_cast<int64_t>(t) * k + lane] = g * scaling;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* zpart, int T, int H,
@@ -284,6 +381,21 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* zpart, 
 
 hipError_t launch_topk(const float* zpart, int S, const float* bias, int T, int E, int k,
                        float scaling, int renorm, int32_t* ids, float* w, hipStream_t stream) {
+  if (T < kTopkBlockTokens) {
+    // Few tokens: a block per token spreads the partial sums over more CUs.
+    switch ((E + 255) / 256) {
+#define MOE_TOPK_CASE(N)                                                                     \
+  case N:                                                                                    \
+    topk_block_kernel<N><<<T, 256, 0, stream>>>(zpart, S, bias, T, E, k, scaling, renorm, ids, \
+                                                w);                                          \
+    break;
+      MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
+#undef MOE_TOPK_CASE
+      default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const int blocks = (T + 3) / 4;
   const int ns = (E + 63) / 64;
   switch (ns) {

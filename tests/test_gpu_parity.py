@@ -87,6 +87,8 @@ SMALL = {
     # enough rows per expert for the 256 x 256 tile shape, ragged last tiles
     "big_tile": dict(T=1100, H=512, E=8, k=4, I=256, Is=128, bias_var=0.5),
     "big_tile_no_shared": dict(T=1500, H=768, E=6, k=3, I=384, Is=0, bias_var=0.2),
+    # enough tokens for the wave-per-token top-k
+    "many_tokens": dict(T=2500, H=256, E=40, k=6, I=64, Is=64, bias_var=0.2),
 }
 
 
@@ -95,6 +97,30 @@ def test_small_full_parity(moe, name):
     wl = synth.WORKLOADS["tiny"].with_(name=name, **SMALL[name])
     out, rep, err, M, *_ = _full_parity(moe, wl)
     gu.note(f"  {name}: max err {err:.3e} M {M:.3e} near-ties {len(rep.near_tie)}")
+
+
+def test_topk_paths_agree(moe):
+    """Below 2048 tokens the top-k runs one block per token, from 2048 one
+    wave per token.  2047 and 2048 tokens give the same router tiling, so
+    the shared tokens must get bit-identical ids and weights."""
+    torch = gu.torch_mod()
+    wl = synth.WORKLOADS["tiny"].with_(name="topk_paths", T=2048, H=256, E=288, k=8, I=64, Is=64)
+    inp = synth.make_inputs(wl)
+    x = gu.to_dev(inp.x)
+    rw = gu.to_dev(inp.router_w)
+    rb = gu.to_dev(inp.router_b)
+    res = {}
+    for T in (2047, 2048):
+        gu.note(f"  moe_route T={T} E=288 k=8")
+        cfg = gu.cfg_of(wl, T=T)
+        ws = moe.alloc_workspace(cfg)
+        ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
+        moe.moe_route(cfg, x[:T], rw, rb, ids, w, ws)
+        torch.cuda.synchronize()
+        res[T] = (ids.cpu().numpy(), w.cpu().numpy())
+    assert np.array_equal(res[2047][0], res[2048][0][:2047])
+    assert np.array_equal(res[2047][1].view(np.uint32), res[2048][1][:2047].view(np.uint32))
 
 
 def test_no_bias(moe):
