@@ -103,19 +103,27 @@ struct Cfg {
   }
 };
 
-// MODE 0: gate/up (+ SwiGLU), MODE 1: down (+ gating weight).
+// MODE 0: gate/up (+ SwiGLU), MODE 1: down (+ gating weight), MODE 2: the
+// router's logits as one dense GEMM over the bf16 planes of its weight.
 template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
 __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   using C = Cfg<BM, BN, BK, WM, WN, S>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
-  const int ntiles = *a.ntiles;
+  const int ntiles = MODE == 2 ? static_cast<int>((a.T + BM - 1) / BM) : *a.ntiles;
   const int u = xcd_remap(blockIdx.x, ntiles * a.NT);
   if (u < 0) return;
   const TileCoord tc = tile_of(u, ntiles, a.NT);
-  const int2 tile = a.tiles[tc.mt];
-  const int e = tile.x, row0 = tile.y;
-  const bool shared = e == a.E;
+  int e, row0;
+  if (MODE == 2) {
+    e = 0;
+    row0 = tc.mt * BM;
+  } else {
+    const int2 tile = a.tiles[tc.mt];
+    e = tile.x;
+    row0 = tile.y;
+  }
+  const bool shared = MODE != 2 && e == a.E;
   const int H = a.H;
 
   // Problem shape of this group.
@@ -123,14 +131,17 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   if (MODE == 0) {
     K = H;
     N = shared ? a.Is : a.I;
-  } else {
+  } else if (MODE == 1) {
     K = shared ? a.Is : a.I;
     N = H;
+  } else {
+    K = H;
+    N = a.Np;
   }
   const int n0 = tc.nt * (MODE == 0 ? BN / 2 : BN);  // first output column
   if (n0 >= N) return;
-  const int rows = shared ? static_cast<int>(min<int64_t>(BM, a.T - row0))
-                          : min(BM, a.offsets[e + 1] - row0);
+  const int rows = (shared || MODE == 2) ? static_cast<int>(min<int64_t>(BM, a.T - row0))
+                                         : min(BM, a.offsets[e + 1] - row0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,7 +153,7 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   const int lrow = lane / C::CH;
   const int pchunk = lane % C::CH;
   const uint16_t* abase;
-  if (MODE == 0)
+  if (MODE != 1)
     abase = a.x;
   else
     abase = shared ? a.h_shared : a.h_routed;
@@ -173,8 +184,11 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
       bmat = up ? (shared ? a.ws_up : a.w_up + static_cast<int64_t>(e) * a.I * H)
                 : (shared ? a.ws_gate : a.w_gate + static_cast<int64_t>(e) * a.I * H);
       mrow = n0 + r0 - (up ? BN / 2 : 0);
-    } else {
+    } else if (MODE == 1) {
       bmat = shared ? a.ws_down : a.w_down + static_cast<int64_t>(e) * H * a.I;
+      mrow = n0 + r0;
+    } else {
+      bmat = a.wsplit;
       mrow = n0 + r0;
     }
 #pragma unroll
@@ -428,6 +442,21 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
               make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
     }
+  } else if (MODE == 2) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      if (row + 32 * mb >= rows) continue;
+      float* zrow = a.zout + static_cast<int64_t>(row0 + row + 32 * mb) * a.Np + n0 +
+                    wn * (BN / WN) + 4 * fh;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& v = acc[mb][nb];
+          *reinterpret_cast<f32x4*>(zrow + 32 * nb + 8 * g) =
+              f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+        }
+    }
   } else {
     uint16_t* out = shared ? a.o_shared : a.o_routed;
 #pragma unroll
@@ -546,6 +575,15 @@ hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStr
   if (shape == kTileBig)
     return launch_one<1, 256, 256, 32, 2, 4, 4>(a, tile_capacity, a.H / 256, stream);
   return launch_one<1, 64, 128, 64, 2, 2, 3>(a, tile_capacity, a.H / 128, stream);
+}
+
+hipError_t launch_router_logits(const ExpertArgs& a, hipStream_t stream) {
+  // Enough 256-row tiles to fill the GPU: 8 waves of 64 x 64; else 64 x 128.
+  if (a.T >= 8192)
+    return launch_one<2, 256, 128, 32, 4, 2, 4>(a, static_cast<int>((a.T + 255) / 256),
+                                               a.Np / 128, stream);
+  return launch_one<2, 64, 128, 64, 2, 2, 3>(a, static_cast<int>((a.T + 63) / 64), a.Np / 128,
+                                             stream);
 }
 
 hipError_t launch_combine(const uint16_t* o_routed, const uint16_t* o_shared,

@@ -35,6 +35,10 @@ struct ExpertArgs {
   uint16_t* o_routed;       // [P][H]
   uint16_t* o_shared;       // [T][H]
   int NT;                   // column tiles (set by the launcher)
+  // Router logits as a GEMM (mode 2): zout[t][n] = x[t] . wsplit[n], n < Np.
+  const uint16_t* wsplit;   // [Np][H] bf16 planes of the router weight, row 3e+p
+  float* zout;              // [T][Np]
+  int Np;                   // rows of wsplit (a multiple of the column tile)
 };
 
 constexpr int kTileBig = 0;    // 256 x 256 tiles
@@ -42,10 +46,18 @@ constexpr int kTileSmall = 1;  // 64 x 128 tiles
 
 // router.hip
 int router_split(int T, int H, int E);
+// Router logits as one bf16 GEMM over the weight's three bf16 planes (from
+// this many tokens on): zpart[t][3e + p] with row stride Np.
+constexpr int kRouterGemmTokens = 1024;
+constexpr int kRouterGemmTileN = 128;  // column tile of that GEMM
+hipError_t launch_router_split(const float* wg, int E, int H, int Np, uint16_t* wsplit,
+                               hipStream_t stream);
+hipError_t launch_router_logits(const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* zpart, int T, int H,
                               int E, int S, hipStream_t stream);
-hipError_t launch_topk(const float* zpart, int S, const float* bias, int T, int E, int k,
-                       float scaling, int renorm, int32_t* ids, float* w, hipStream_t stream);
+hipError_t launch_topk(const float* zpart, int S, int64_t ld, const float* bias, int T, int E,
+                       int k, float scaling, int renorm, int32_t* ids, float* w,
+                       hipStream_t stream);
 
 // permute.hip; ev (optional) receives three events, one before each kernel.
 hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, int with_shared,

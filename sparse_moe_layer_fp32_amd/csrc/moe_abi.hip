@@ -35,11 +35,14 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   int64_t T, P;
   int H, E, k, I, Is;
-  int S;         // router split-K factor
+  int S;         // partials per logit: k splits, or 3 weight planes (router GEMM form)
+  int rgemm;     // router logits as one GEMM over the weight planes
+  int Np;        // router GEMM: rows of the plane matrix (3E rounded up to the column tile)
+  int64_t zld;   // row stride of the partial logits
   int C;         // permutation chunks, padded to a multiple of 4
   int shape;     // expert GEMM tile shape (kTileBig / kTileSmall)
   int tile_cap;  // capacity of the GEMM tile list
-  size_t zpart, ids, w, rank, hist, base, offsets, sorted, pos, wsorted, tiles, ntiles, h, o, total;
+  size_t zpart, wsplit, ids, w, rank, hist, base, offsets, sorted, pos, wsorted, tiles, ntiles, h, o, total;
 };
 
 moe_status validate(const moe_config* c) {
@@ -77,7 +80,10 @@ void make_plan(const moe_config* c, Plan* p) {
   p->I = c->inter;
   p->Is = c->inter_shared;
   const int T = static_cast<int>(p->T);
-  p->S = p->T > 0 ? moe::router_split(T, p->H, p->E) : 1;
+  p->rgemm = p->T >= moe::kRouterGemmTokens;
+  p->Np = (3 * p->E + moe::kRouterGemmTileN - 1) / moe::kRouterGemmTileN * moe::kRouterGemmTileN;
+  p->S = p->rgemm ? 3 : (p->T > 0 ? moe::router_split(T, p->H, p->E) : 1);
+  p->zld = p->rgemm ? p->Np : static_cast<int64_t>(p->E) * p->S;
   p->C = moe::permute_hist_stride(static_cast<int>(p->P));  // padded chunk count
   p->shape = moe::experts_pick_shape(p->T, static_cast<int>(p->P), p->E, p->H, p->I, p->Is);
   p->tile_cap = moe::experts_tile_capacity(p->T, static_cast<int>(p->P), p->E, p->Is > 0, p->shape);
@@ -88,7 +94,8 @@ void make_plan(const moe_config* c, Plan* p) {
     return at;
   };
   const size_t P = static_cast<size_t>(p->P), T64 = static_cast<size_t>(p->T);
-  p->zpart = take(static_cast<size_t>(p->S) * T64 * p->E * 4);
+  p->zpart = take(static_cast<size_t>(p->zld) * T64 * 4);
+  p->wsplit = take(p->rgemm ? static_cast<size_t>(p->Np) * p->H * 2 : 0);
   p->ids = take(P * 4);
   p->w = take(P * 4);
   p->rank = take(P * 4);
@@ -136,9 +143,23 @@ moe_status route_impl(const Plan& p, const moe_config* c, const uint16_t* x, con
   float* zpart = at<float>(ws, p.zpart);
   const int T = static_cast<int>(p.T);
   if (ev) hipEventRecord(ev[0], stream);
-  MOE_CHECK_LAUNCH(moe::launch_router_gemm(x, rw, zpart, T, p.H, p.E, p.S, stream), "router gemm");
+  if (p.rgemm) {
+    uint16_t* wsplit = at<uint16_t>(ws, p.wsplit);
+    MOE_CHECK_LAUNCH(moe::launch_router_split(rw, p.E, p.H, p.Np, wsplit, stream), "router split");
+    moe::ExpertArgs g{};
+    g.x = x;
+    g.T = p.T;
+    g.H = p.H;
+    g.wsplit = wsplit;
+    g.zout = zpart;
+    g.Np = p.Np;
+    MOE_CHECK_LAUNCH(moe::launch_router_logits(g, stream), "router gemm");
+  } else {
+    MOE_CHECK_LAUNCH(moe::launch_router_gemm(x, rw, zpart, T, p.H, p.E, p.S, stream),
+                     "router gemm");
+  }
   if (ev) hipEventRecord(ev[1], stream);
-  MOE_CHECK_LAUNCH(moe::launch_topk(zpart, p.S, rb, T, p.E, p.k, c->routed_scaling,
+  MOE_CHECK_LAUNCH(moe::launch_topk(zpart, p.S, p.zld, rb, T, p.E, p.k, c->routed_scaling,
                                     c->renormalize ? 1 : 0, ids, w, stream),
                    "top-k");
   return MOE_OK;

@@ -193,14 +193,16 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return a > b ? a : b;
 }
 
-// Sum of the S split partials of one logit, in split order (S a power of
-// two <= 32; the partials of one logit are contiguous).
+// Sum of the S partials of one logit, in order (S a power of two <= 32 for
+// k splits, or 3 for the weight planes; the partials of one logit are
+// contiguous).
 __device__ __forceinline__ float sum_splits(const float* p, int S) {
   if (S == 1) return p[0];
   if (S == 2) {
     const float2 a = *reinterpret_cast<const float2*>(p);
     return a.x + a.y;
   }
+  if (S == 3) return (p[0] + p[1]) + p[2];  // the three weight planes, hi + mid + lo
   f32x4 v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -216,7 +218,8 @@ __device__ __forceinline__ float sum_splits(const float* p, int S) {
 
 template <int NS>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpart, int S,
-                                                   const float* __restrict__ bias, int T, int E,
+                                                   int64_t ld, const float* __restrict__ bias,
+                                                   int T, int E,
                                                    int k, float scaling, int renorm,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpa
     z[i] = 0.f;
     key[i] = 0;  // below every real key: never selected
     if (e < E) {
-      z[i] = sum_splits(zpart + (static_cast<int64_t>(t) * E + e) * S, S);
+      z[i] = sum_splits(zpart + static_cast<int64_t>(t) * ld + static_cast<int64_t>(e) * S, S);
       float kv = sigmoid_f32(z[i]) + (bias ? bias[e] : 0.f);
       if (kv != kv) kv = -INFINITY;  // non-finite input: rank last, stay in range
       key[i] = (static_cast<uint64_t>(orderable(kv)) << 32) |
@@ -280,6 +283,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpa
 // those of topk_kernel, so the two kernels give identical results.
 template <int NS>
 __global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict__ zpart, int S,
+                                                         int64_t ld,
                                                          const float* __restrict__ bias, int T,
                                                          int E, int k, float scaling, int renorm,
                                                          int32_t* __restrict__ ids,
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict
     z[i] = 0.f;
     key[i] = 0;
     if (e < E) {
-      z[i] = sum_splits(zpart + (static_cast<int64_t>(t) * E + e) * S, S);
+      z[i] = sum_splits(zpart + static_cast<int64_t>(t) * ld + static_cast<int64_t>(e) * S, S);
       float kv = sigmoid_f32(z[i]) + (bias ? bias[e] : 0.f);
       if (kv != kv) kv = -INFINITY;
       key[i] = (static_cast<uint64_t>(orderable(kv)) << 32) |
@@ -370,6 +374,39 @@ __global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict
   }
 }
 
+// The three bf16 planes of the router weight for the GEMM form of the
+// logits: wsplit[3e + p][h] = plane p of wg[e][h] (split3 above), rows 3E ..
+// Np-1 zero.  One thread per 8 consecutive weights.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wg, int E,
+                                                           int H, int Np,
+                                                           uint16_t* __restrict__ wsplit) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int per_row = H / 8;
+  const int64_t real = static_cast<int64_t>(E) * per_row;
+  const int64_t pad = static_cast<int64_t>(Np - 3 * E) * per_row;
+  if (i < real) {
+    const int e = static_cast<int>(i / per_row);
+    const int h = static_cast<int>(i - static_cast<int64_t>(e) * per_row) * 8;
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(wg + static_cast<int64_t>(e) * H + h);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(wg + static_cast<int64_t>(e) * H + h + 4);
+    uint32_t pl[3][8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) split3(q < 4 ? w0[q] : w1[q - 4], pl[0][q], pl[1][q], pl[2][q]);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      u32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = pl[p][2 * q] | (pl[p][2 * q + 1] << 16);
+      *reinterpret_cast<u32x4*>(wsplit + static_cast<int64_t>(3 * e + p) * H + h) = v;
+    }
+  } else if (i < real + pad) {
+    const int64_t j = i - real;
+    const int n = 3 * E + static_cast<int>(j / per_row);
+    const int h = static_cast<int>(j % per_row) * 8;
+    *reinterpret_cast<u32x4*>(wsplit + static_cast<int64_t>(n) * H + h) = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* zpart, int T, int H,
@@ -379,15 +416,16 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* zpart, 
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* zpart, int S, const float* bias, int T, int E, int k,
-                       float scaling, int renorm, int32_t* ids, float* w, hipStream_t stream) {
+hipError_t launch_topk(const float* zpart, int S, int64_t ld, const float* bias, int T, int E,
+                       int k, float scaling, int renorm, int32_t* ids, float* w,
+                       hipStream_t stream) {
   if (T < kTopkBlockTokens) {
     // Few tokens: a block per token spreads the partial sums over more CUs.
     switch ((E + 255) / 256) {
 #define MOE_TOPK_CASE(N)                                                                     \
   case N:                                                                                    \
-    topk_block_kernel<N><<<T, 256, 0, stream>>>(zpart, S, bias, T, E, k, scaling, renorm, ids, \
-                                                w);                                          \
+    topk_block_kernel<N><<<T, 256, 0, stream>>>(zpart, S, ld, bias, T, E, k, scaling, renorm, \
+                                                ids, w);                                          \
     break;
       MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
 #undef MOE_TOPK_CASE
@@ -401,7 +439,8 @@ hipError_t launch_topk(const float* zpart, int S, const float* bias, int T, int 
   switch (ns) {
 #define MOE_TOPK_CASE(N) \
   case N:                \
-    topk_kernel<N><<<blocks, 256, 0, stream>>>(zpart, S, bias, T, E, k, scaling, renorm, ids, w); \
+    topk_kernel<N><<<blocks, 256, 0, stream>>>(zpart, S, ld, bias, T, E, k, scaling, renorm, ids, \
+                                               w); \
     break;
     MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4) MOE_TOPK_CASE(5)
     MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8) MOE_TOPK_CASE(9) MOE_TOPK_CASE(10)
@@ -411,6 +450,15 @@ hipError_t launch_topk(const float* zpart, int S, const float* bias, int T, int 
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_split(const float* wg, int E, int H, int Np, uint16_t* wsplit,
+                               hipStream_t stream) {
+  const int64_t threads = static_cast<int64_t>(Np - 2 * E) * (H / 8);  // E real rows + pad
+  if (threads <= 0) return hipSuccess;
+  router_split_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, stream>>>(
+      wg, E, H, Np, wsplit);
   return hipGetLastError();
 }
 
