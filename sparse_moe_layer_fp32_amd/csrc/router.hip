@@ -276,55 +276,44 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpa
   }
 }
 
-// Few tokens, many partials: one 256-thread block per token, thread i
-// holding experts i, i + 256, ...  Each wave selects its own top k (as
-// above); wave 0 then selects the top k of the 4k candidates.  Every expert
-// of the global top k is in its wave's top k, and the keys and scores are
-// those of topk_kernel, so the two kernels give identical results.
-template <int NS>
-__global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict__ zpart, int S,
-                                                         int64_t ld,
-                                                         const float* __restrict__ bias, int T,
-                                                         int E, int k, float scaling, int renorm,
-                                                         int32_t* __restrict__ ids,
-                                                         float* __restrict__ w) {
-  __shared__ uint64_t cand_key[4][kMaxTopK];
-  __shared__ float cand_z[4][kMaxTopK];
+// Few tokens, many partials: one block per token with one thread per expert
+// (64 ceil(E / 64) threads), so every logit's partials are requested at
+// once.  Each wave selects its own top k (as above); wave 0 then selects
+// the top k of the waves' candidates.  Every expert of the global top k is
+// in its wave's top k, and the keys and scores are those of topk_kernel, so
+// the two kernels give identical results.
+constexpr int TKB_MAX_WAVES = kMaxExperts / 64;
+constexpr int TKB_PER_LANE = TKB_MAX_WAVES * kMaxTopK / 64;  // merge candidates per lane
+
+__global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restrict__ zpart, int S,
+                                                          int64_t ld,
+                                                          const float* __restrict__ bias, int T,
+                                                          int E, int k, float scaling,
+                                                          int renorm, int32_t* __restrict__ ids,
+                                                          float* __restrict__ w) {
+  __shared__ uint64_t cand_key[TKB_MAX_WAVES][kMaxTopK];
+  __shared__ float cand_z[TKB_MAX_WAVES][kMaxTopK];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
   const int t = blockIdx.x;
+  const int e = tid;
 
-  float z[NS];
-  uint64_t key[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int e = tid + 256 * i;
-    z[i] = 0.f;
-    key[i] = 0;
-    if (e < E) {
-      z[i] = sum_splits(zpart + static_cast<int64_t>(t) * ld + static_cast<int64_t>(e) * S, S);
-      float kv = sigmoid_f32(z[i]) + (bias ? bias[e] : 0.f);
-      if (kv != kv) kv = -INFINITY;
-      key[i] = (static_cast<uint64_t>(orderable(kv)) << 32) |
-               (0xFFFFFFFFu - static_cast<uint32_t>(e));
-    }
+  float z = 0.f;
+  uint64_t key = 0;
+  if (e < E) {
+    z = sum_splits(zpart + static_cast<int64_t>(t) * ld + static_cast<int64_t>(e) * S, S);
+    float kv = sigmoid_f32(z) + (bias ? bias[e] : 0.f);
+    if (kv != kv) kv = -INFINITY;
+    key = (static_cast<uint64_t>(orderable(kv)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
   }
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      if (key[i] > best) best = key[i];
-    const uint64_t win = wave_max_u64(best);
+    const uint64_t win = wave_max_u64(key);
     float zw = 0.f;
     if (win != 0) {  // 0: this wave has no keys left
-      const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(win));
-      const int owner = id & 63, slot = id >> 8;
-#pragma unroll
-      for (int i = 0; i < NS; ++i)
-        if (i == slot) {
-          zw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z[i]), owner));
-          if (lane == owner) key[i] = 0;
-        }
+      const int owner = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(win)) & 63;
+      zw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), owner));
+      if (lane == owner) key = 0;
     }
     if (lane == 0) {
       cand_key[wave][j] = win;
@@ -334,15 +323,16 @@ __global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict
   __syncthreads();
   if (wave != 0) return;
 
-  // Lane l holds candidates l and l + 64 of the 4k (wave-major order).
-  uint64_t ck[2];
-  float cz[2];
+  // Lane l holds candidates l, l + 64, ... of the nwaves * k (wave-major).
+  const int ncand = nwaves * k;
+  uint64_t ck[TKB_PER_LANE];
+  float cz[TKB_PER_LANE];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < TKB_PER_LANE; ++h) {
     const int c = lane + 64 * h;
     ck[h] = 0;
     cz[h] = 0.f;
-    if (c < 4 * k) {
+    if (c < ncand) {
       ck[h] = cand_key[c / k][c % k];
       cz[h] = cand_z[c / k][c % k];
     }
@@ -350,16 +340,24 @@ __global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict
   int my_id = 0;
   float my_s = 0.f;
   for (int j = 0; j < k; ++j) {
-    const uint64_t best = ck[0] > ck[1] ? ck[0] : ck[1];
+    uint64_t best = 0;
+#pragma unroll
+    for (int h = 0; h < TKB_PER_LANE; ++h) best = ck[h] > best ? ck[h] : best;
     const uint64_t win = wave_max_u64(best);
     const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(win));
-    // The holder of the winning key publishes its logit.
-    const int h = ck[1] == win ? 1 : 0;
-    const bool mine = ck[h] == win;
+    // The holder of the winning key publishes its logit and retires it.
+    float zmine = 0.f;
+    bool mine = false;
+#pragma unroll
+    for (int h = 0; h < TKB_PER_LANE; ++h)
+      if (ck[h] == win) {
+        zmine = cz[h];
+        ck[h] = 0;
+        mine = true;
+      }
     const uint64_t mask = __ballot(mine);
     const int holder = __builtin_ctzll(mask);
-    const float zsel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h ? cz[1] : cz[0]), holder));
-    if (mine) ck[h] = 0;
+    const float zsel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zmine), holder));
     if (lane == j) {
       my_id = id;
       my_s = sigmoid_f32(zsel);
@@ -421,17 +419,9 @@ hipError_t launch_topk(const float* zpart, int S, int64_t ld, const float* bias,
                        hipStream_t stream) {
   if (T < kTopkBlockTokens) {
     // Few tokens: a block per token spreads the partial sums over more CUs.
-    switch ((E + 255) / 256) {
-#define MOE_TOPK_CASE(N)                                                                     \
-  case N:                                                                                    \
-    topk_block_kernel<N><<<T, 256, 0, stream>>>(zpart, S, ld, bias, T, E, k, scaling, renorm, \
-                                                ids, w);                                          \
-    break;
-      MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
-#undef MOE_TOPK_CASE
-      default:
-        return hipErrorInvalidValue;
-    }
+    const int threads = (E + 63) / 64 * 64;
+    topk_block_kernel<<<T, threads, 0, stream>>>(zpart, S, ld, bias, T, E, k, scaling, renorm,
+                                                 ids, w);
     return hipGetLastError();
   }
   const int blocks = (T + 3) / 4;
