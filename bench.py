@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--weight-copies", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the second workloads (Step-3 MoE shape, dense FFN)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES five times (to scale HBM "
                          "traffic counters) and exit")
@@ -214,7 +216,7 @@ def measure(wl, moe, synth, experts_host, copies, steps, warmup):
 
     x = dev(synth.gen_x(wl))
     rw_h, rb_h, _ = synth.gen_router(wl)
-    rw, rb = dev(rw_h), dev(rb_h)
+    rw, rb = dev(rw_h), (dev(rb_h) if wl.use_bias else None)
     cfg = moe.make_config(wl.T, wl.H, wl.E, wl.k, wl.I, wl.Is, wl.routed_scaling,
                           wl.renormalize, wl.limit, wl.limit_shared)
     ws = moe.alloc_workspace(cfg)
@@ -275,6 +277,35 @@ def measure(wl, moe, synth, experts_host, copies, steps, warmup):
     return out, ids_h
 
 
+def measure_dense(wl, moe, synth, steps, warmup):
+    """The dense SwiGLU FFN (moe_dense_forward) on its workload: ms/step and
+    the MFMA rate of its 6*T*H*I FLOPs."""
+    import numpy as np
+    import torch
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    inp = synth.make_inputs(wl)
+    x, wg, wu, wd = dev(inp.x), dev(inp.ws_gate), dev(inp.ws_up), dev(inp.ws_down)
+    cfg = moe.make_dense_config(wl.T, wl.H, wl.Is, wl.limit_shared)
+    ws = moe.alloc_dense_workspace(cfg)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        moe.moe_dense_forward(cfg, x, wg, wu, wd, y, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        moe.moe_dense_forward(cfg, x, wg, wu, wd, y, ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flop = 6.0 * wl.T * wl.H * wl.Is
+    tf = flop / (ms * 1e-3) * 1e-12
+    return dict(tokens=wl.T, hidden=wl.H, inter=wl.Is, ms_per_step=round(ms, 5),
+                tokens_per_s=round(wl.T / (ms * 1e-3), 1), tflops=round(tf, 2),
+                frac_mfma=round(tf / BF16_PEAK_TFLOPS, 4))
+
+
 def roofline(wl, res, bound):
     g = res["gateup"]
     if bound == "hbm":
@@ -290,15 +321,21 @@ def roofline(wl, res, bound):
 
 
 def cpu_baseline(wl, inp):
+    """The oracle on the whole decode batch, repeated until at least 10 s of
+    CPU time have passed (capped at 30 s)."""
     import oracle
     threads = oracle.default_threads()
     cfg = oracle.cfg_of(wl)
-    t0 = time.perf_counter()
-    oracle.forward(cfg, inp, threads=threads)
-    dt = time.perf_counter() - t0
-    return dict(value=round(wl.T / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"all {wl.T} tokens of the {wl.name} workload (double-precision "
-                       f"per-token oracle, {dt:.1f} s wall)")
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(cfg, inp, threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or dt * (reps + 1) / reps > 30.0:
+            break
+    return dict(value=round(reps * wl.T / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{reps} passes over all {wl.T} tokens of the {wl.name} workload "
+                       f"(double-precision per-token oracle, {dt:.1f} s wall)")
 
 
 def main():
@@ -368,6 +405,29 @@ def main():
                               roofline=roofline(pw, pres, "mfma"), stage_ms=pres["stage_ms"],
                               experts_used=pres["experts_used"])
         log(f"[bench] prefill: {pres['ms_per_step']:.4f} ms/step, stages {pres['stage_ms']}")
+
+    if wl.name == "decode" and not args.no_secondary and not args.no_extra:
+        # Second workloads on the same kernels: the predecessor Step-3's MoE shape and the
+        # dense SwiGLU FFN of the first layers.
+        rec["workloads"] = {}
+        sw = synth.WORKLOADS["step3"]
+        log(f"[bench] step3 T={sw.T} (H {sw.H}, E {sw.E}, k {sw.k}, I {sw.I})")
+        s_host = synth.gen_experts(sw)
+        s_dev = [tuple(dev(a) for a in s_host)]
+        del s_host
+        sres, _ = measure(sw, moe, synth, None, s_dev, 10, 3)
+        rec["workloads"]["step3"] = dict(
+            tokens=sw.T, hidden=sw.H, experts=sw.E, top_k=sw.k, inter=sw.I, inter_shared=sw.Is,
+            ms_per_step=round(sres["ms_per_step"], 5), tokens_per_s=round(sres["tokens_per_s"], 1),
+            tflops=round(sres["tflops"], 2), frac_mfma=round(sres["frac_mfma"], 4),
+            experts_used=sres["experts_used"], stage_ms=sres["stage_ms"])
+        log(f"[bench] step3: {sres['ms_per_step']:.4f} ms/step")
+        del s_dev
+        torch.cuda.empty_cache()
+        dw = synth.WORKLOADS["dense"]
+        log(f"[bench] dense FFN T={dw.T} I={dw.Is}")
+        rec["workloads"]["dense_ffn"] = measure_dense(dw, moe, synth, 10, 3)
+        log(f"[bench] dense: {rec['workloads']['dense_ffn']['ms_per_step']:.4f} ms/step")
 
     if not args.no_cpu and wl.name in ("decode", "tiny"):
         log("[bench] CPU oracle baseline")

@@ -170,6 +170,36 @@ enum {
 };
 moe_status moe_workspace_view(const moe_config* cfg, int which, size_t* offset, size_t* bytes);
 
+/* ---- Dense SwiGLU FFN ----------------------------------------------------
+ * The FFN of Step-3.5-Flash's first three layers, which are dense (sglang-jax
+ * issue, "Model configuration", MLP bullet: intermediate 11264; "Reuse map":
+ * first-k dense + MoE layers; llm-atlas model card, "Raw config fields":
+ * intermediate_size).  The same clamped SwiGLU MLP as one expert above, applied to every
+ * token:  y_t = W_down (SiLU(g) * u),  g = W_gate x_t,  u = W_up x_t, with
+ * g = min(g, L), u = clamp(u, -L, L) for L > 0.  It runs on the grouped
+ * expert GEMMs with a single group of all T tokens.
+ *   x      [T][H] bf16;  w_gate, w_up [I][H] bf16;  w_down [H][I] bf16
+ *   y      out [T][H] bf16
+ *   ws     device workspace of ws_bytes >= moe_dense_workspace_size(cfg)
+ * Limits: hidden % 128 == 0; inter % 64 == 0, inter >= 64; tokens *
+ * max(hidden, inter) < 2^32; pointers 16-byte aligned.  Conventions as above
+ * (tokens == 0 launches nothing; x and y may then be NULL). */
+typedef struct {
+  int64_t tokens;     /* T >= 0                                    */
+  int32_t hidden;     /* H, hidden_size (4096)                     */
+  int32_t inter;      /* I, intermediate_size (11264)              */
+  float swiglu_limit; /* swiglu_limits[layer] (0.0 for these layers); <= 0: none */
+  int32_t reserved;   /* must be 0                                 */
+} moe_dense_config;
+
+/* Workspace bytes for moe_dense_forward; 0 for an invalid configuration. */
+size_t moe_dense_workspace_size(const moe_dense_config* cfg);
+
+moe_status moe_dense_forward(const moe_dense_config* cfg, const uint16_t* x,
+                             const uint16_t* w_gate, const uint16_t* w_up,
+                             const uint16_t* w_down, uint16_t* y, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

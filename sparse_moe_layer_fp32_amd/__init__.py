@@ -47,6 +47,15 @@ def make_config(tokens, hidden=4096, num_experts=288, top_k=8, inter=1280, inter
                       float(swiglu_limit), float(swiglu_limit_shared))
 
 
+class moe_dense_config(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("swiglu_limit", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
+def make_dense_config(tokens, hidden=4096, inter=11264, swiglu_limit=0.0) -> moe_dense_config:
+    return moe_dense_config(int(tokens), int(hidden), int(inter), float(swiglu_limit), 0)
+
+
 _lib = None
 
 
@@ -69,15 +78,20 @@ def load_library():
     lib.moe_forward.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_forward_timed.argtypes = lib.moe_forward.argtypes + [ctypes.POINTER(vp), ctypes.c_int]
     lib.moe_workspace_view.argtypes = [cp, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    dp = ctypes.POINTER(moe_dense_config)
+    lib.moe_dense_workspace_size.argtypes = [dp]
+    lib.moe_dense_workspace_size.restype = sz
+    lib.moe_dense_forward.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     for f in ("moe_route", "moe_permute", "moe_forward", "moe_forward_timed",
-              "moe_workspace_view"):
+              "moe_workspace_view", "moe_dense_forward"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
 
 
 EXPORTED = ("moe_workspace_size", "moe_last_error", "moe_route", "moe_permute", "moe_forward",
-            "moe_forward_timed", "moe_workspace_view")
+            "moe_forward_timed", "moe_workspace_view", "moe_dense_workspace_size",
+            "moe_dense_forward")
 
 
 # ------------------------------------------------------------------ helpers
@@ -242,3 +256,28 @@ def forward(cfg: moe_config, x, weights: MoeWeights, y=None, ws=None, topk_ids=N
                 weights.w_down, weights.ws_gate if sh else None, weights.ws_up if sh else None,
                 weights.ws_down if sh else None, y, topk_ids, topk_w, ws, stream)
     return y
+
+
+# ------------------------------------------------------------------ dense FFN
+
+def moe_dense_workspace_size(cfg: moe_dense_config) -> int:
+    n = load_library().moe_dense_workspace_size(ctypes.byref(cfg))
+    if n == 0:
+        raise MoeError(MOE_ERR_INVALID_ARG, moe_last_error())
+    return int(n)
+
+
+def alloc_dense_workspace(cfg: moe_dense_config, device=None):
+    torch = _torch()
+    return torch.empty(moe_dense_workspace_size(cfg), dtype=torch.uint8,
+                       device=device or torch.device("cuda"))
+
+
+def moe_dense_forward(cfg, x, w_gate, w_up, w_down, y, ws, stream=None):
+    lib = load_library()
+    _check(lib.moe_dense_forward(ctypes.byref(cfg), _ptr(x, _bf16(), "x", cfg.tokens == 0),
+                                 _ptr(w_gate, _bf16(), "w_gate"), _ptr(w_up, _bf16(), "w_up"),
+                                 _ptr(w_down, _bf16(), "w_down"),
+                                 _ptr(y, _bf16(), "y", cfg.tokens == 0),
+                                 _ptr(ws, None, "ws"), ws.numel() * ws.element_size(),
+                                 _stream(stream)))

@@ -67,6 +67,8 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, i
                           hipEvent_t* ev);
 
 hipError_t launch_fill_zero(int32_t* p, int n, hipStream_t stream);
+hipError_t launch_dense_tiles(int2* tiles, int32_t* ntiles, int64_t T, int bm, int group,
+                              hipStream_t stream);
 int permute_chunk(int P);        // pairs per rank/histogram chunk (at most 64 chunks)
 int permute_hist_stride(int P);  // histogram row stride: chunk count rounded up to 4
 

@@ -252,9 +252,104 @@ moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* rou
   return ok();
 }
 
+// ---- dense SwiGLU FFN: the expert GEMMs with one group of all T rows.
+struct DensePlan {
+  int64_t T;
+  int H, I;
+  int shape, tile_cap;
+  size_t tiles, ntiles, h, total;
+};
+
+moe_status validate_dense(const moe_dense_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->tokens < 0) return fail(MOE_ERR_INVALID_ARG, "tokens < 0 (%lld)", (long long)c->tokens);
+  if (c->hidden <= 0 || c->inter <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "non-positive size (hidden %d, inter %d)", c->hidden, c->inter);
+  if (c->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved field must be 0");
+  if (c->hidden % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden %d is not a multiple of 128", c->hidden);
+  if (c->inter % 64) return fail(MOE_ERR_UNSUPPORTED, "inter %d not a multiple of 64", c->inter);
+  if (c->tokens * static_cast<int64_t>(std::max(c->hidden, c->inter)) >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "tokens * max(hidden, inter) must be < 2^32");
+  return MOE_OK;
+}
+
+void make_dense_plan(const moe_dense_config* c, DensePlan* p) {
+  p->T = c->tokens;
+  p->H = c->hidden;
+  p->I = c->inter;
+  // One group of T rows: big tiles once the rows outnumber a few tiles.
+  const bool fits = p->H % 256 == 0 && p->I % 128 == 0;
+  p->shape = (fits && p->T >= 1024) ? moe::kTileBig : moe::kTileSmall;
+  const int bm = moe::experts_tile_rows(p->shape);
+  p->tile_cap = static_cast<int>(std::max<int64_t>(1, (p->T + bm - 1) / bm));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  p->tiles = take(static_cast<size_t>(p->tile_cap) * 8);
+  p->ntiles = take(16);
+  p->h = take(static_cast<size_t>(p->T) * p->I * 2);
+  p->total = off;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t moe_dense_workspace_size(const moe_dense_config* cfg) {
+  if (validate_dense(cfg) != MOE_OK) return 0;
+  DensePlan p;
+  make_dense_plan(cfg, &p);
+  return p.total;
+}
+
+moe_status moe_dense_forward(const moe_dense_config* cfg, const uint16_t* x,
+                             const uint16_t* w_gate, const uint16_t* w_up,
+                             const uint16_t* w_down, uint16_t* y, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  moe_status st = validate_dense(cfg);
+  if (st) return st;
+  if (!w_gate || !w_up || !w_down || (cfg->tokens > 0 && (!x || !y)))
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  const void* ptrs[] = {x, w_gate, w_up, w_down, y};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MOE_ERR_UNSUPPORTED, "pointer %p not 16-byte aligned", q);
+  DensePlan p;
+  make_dense_plan(cfg, &p);
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  if (ws_bytes < p.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, p.total);
+  if (p.T == 0) return ok();
+
+  // The MLP is the expert GEMMs' shared group (group index E = 0): no routed
+  // experts, weight 1.0, its output written straight into y.
+  moe::ExpertArgs g{};
+  g.x = x;
+  g.k = 1;
+  g.T = p.T;
+  g.H = p.H;
+  g.I = 0;
+  g.Is = p.I;
+  g.E = 0;
+  g.ws_gate = w_gate;
+  g.ws_up = w_up;
+  g.ws_down = w_down;
+  g.limit_shared = cfg->swiglu_limit;
+  g.tiles = at<int2>(ws, p.tiles);
+  g.ntiles = at<int32_t>(ws, p.ntiles);
+  g.h_shared = at<uint16_t>(ws, p.h);
+  g.o_shared = y;
+  MOE_CHECK_LAUNCH(moe::launch_dense_tiles(at<int2>(ws, p.tiles), at<int32_t>(ws, p.ntiles), p.T,
+                                           moe::experts_tile_rows(p.shape), 0, stream),
+                   "dense tile list");
+  MOE_CHECK_LAUNCH(moe::launch_gateup(g, p.shape, p.tile_cap, stream), "dense gate/up gemm");
+  MOE_CHECK_LAUNCH(moe::launch_down(g, p.shape, p.tile_cap, stream), "dense down gemm");
+  return ok();
+}
 
 size_t moe_workspace_size(const moe_config* cfg) {
   if (validate(cfg) != MOE_OK) return 0;

@@ -287,6 +287,14 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   if (w_sorted) w_sorted[i] = topk_w[p];
 }
 
+// Tile list of a single group of T rows (the dense FFN): (group, first row).
+__global__ void dense_tiles_kernel(int2* __restrict__ tiles, int32_t* __restrict__ ntiles, int n,
+                                   int bm, int group) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) tiles[i] = make_int2(group, i * bm);
+  if (i == 0) *ntiles = n;
+}
+
 __global__ void fill_zero_kernel(int32_t* __restrict__ p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -304,6 +312,13 @@ int permute_chunk(int P) {
   // At most 64 chunks, each a multiple of the LDS staging size.
   const int per = (P + 63) / 64;
   return std::max(kSmallPairs, (per + kSmallPairs - 1) / kSmallPairs * kSmallPairs);
+}
+
+hipError_t launch_dense_tiles(int2* tiles, int32_t* ntiles, int64_t T, int bm, int group,
+                              hipStream_t stream) {
+  const int n = static_cast<int>((T + bm - 1) / bm);
+  dense_tiles_kernel<<<(std::max(n, 1) + 255) / 256, 256, 0, stream>>>(tiles, ntiles, n, bm, group);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(int32_t* p, int n, hipStream_t stream) {

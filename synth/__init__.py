@@ -137,6 +137,7 @@ class Workload:
     hot_experts: int = 0         # this many experts get bias == hot_bias
     hot_bias: float = 2.0
     x_scale: tuple | None = None  # per-token factor ~ U(lo, hi) on x
+    use_bias: bool = True        # False: no router bias (NULL pointer)
     seed: int = 0
 
     @property
@@ -153,6 +154,14 @@ WORKLOADS = {
     "prefill": Workload("prefill", T=8192),
     "skewed": Workload("skewed", T=4096, hot_experts=16, hot_bias=2.0, limit=7.0, limit_shared=0.0),
     "long": Workload("long", T=32768, bias_var=0.3, x_scale=(0.5, 2.0)),
+    # The predecessor Step-3's MoE shape (model card comparison table): H 7168, 48 experts,
+    # top-3, I = shared 5120, norm_expert_weight false; no router bias or scaling is listed
+    # for it, so none (scaling 1.0).
+    "step3": Workload("step3", T=4096, H=7168, E=48, k=3, I=5120, Is=5120, routed_scaling=1.0,
+                      renormalize=False, use_bias=False),
+    # The dense SwiGLU FFN of Step-3.5-Flash's first layers (intermediate_size 11264): no
+    # router and no routed experts (E = k = I = 0); the MLP's weights are the "shared" ones.
+    "dense": Workload("dense", T=8192, E=0, k=0, I=0, Is=11264),
 }
 
 
@@ -181,6 +190,8 @@ def gen_x(wl: Workload) -> np.ndarray:
 
 
 def gen_router(wl: Workload):
+    if wl.E == 0:
+        return np.zeros((0, wl.H), np.float32), None, None
     wg = normal_f32(wl.seed, T_WG, wl.E * wl.H, math.sqrt(1.0 / wl.H)).reshape(wl.E, wl.H)
     b = normal_f32(wl.seed, T_B, wl.E, math.sqrt(wl.bias_var))
     hot = None
@@ -194,7 +205,7 @@ def gen_experts(wl: Workload):
     E, I, H, Is = wl.E, wl.I, wl.H, wl.Is
     wg = normal_bf16(wl.seed, T_WGATE, E * I * H, math.sqrt(1.0 / H)).reshape(E, I, H)
     wu = normal_bf16(wl.seed, T_WUP, E * I * H, math.sqrt(1.0 / H)).reshape(E, I, H)
-    wd = normal_bf16(wl.seed, T_WDOWN, E * H * I, math.sqrt(1.0 / I)).reshape(E, H, I)
+    wd = normal_bf16(wl.seed, T_WDOWN, E * H * I, math.sqrt(1.0 / max(I, 1))).reshape(E, H, I)
     if Is > 0:
         sg = normal_bf16(wl.seed, T_WSGATE, Is * H, math.sqrt(1.0 / H)).reshape(Is, H)
         su = normal_bf16(wl.seed, T_WSUP, Is * H, math.sqrt(1.0 / H)).reshape(Is, H)
@@ -211,6 +222,8 @@ def make_inputs(wl: Workload, experts=None) -> Inputs:
     for the same (H, E, I, Is, seed) to avoid regenerating 9 GB of weights."""
     x = gen_x(wl)
     wg, b, hot = gen_router(wl)
+    if not wl.use_bias:
+        b = None
     if experts is None:
         experts = gen_experts(wl)
     return Inputs(wl, x, wg, b, *experts, hot=hot)

@@ -101,3 +101,50 @@ def test_null_pointers_and_small_workspace():
     off, nb = ctypes.c_size_t(), ctypes.c_size_t()
     assert lib.moe_workspace_view(ctypes.byref(cfg), 99, ctypes.byref(off),
                                   ctypes.byref(nb)) == moe.MOE_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ dense FFN
+
+def test_dense_config_layout_and_workspace():
+    assert ctypes.sizeof(moe.moe_dense_config) == 24
+    assert moe.moe_dense_config.swiglu_limit.offset == 16
+    s = [moe.moe_dense_workspace_size(moe.make_dense_config(T)) for T in (0, 64, 8192)]
+    assert 0 < s[0] < s[1] < s[2]
+    assert s[2] >= 8192 * 11264 * 2  # the bf16 SwiGLU activations
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(inter=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(tokens=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(hidden=4000), moe.MOE_ERR_UNSUPPORTED),
+    (dict(inter=11200 + 10), moe.MOE_ERR_UNSUPPORTED),
+    (dict(tokens=2**20), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_dense_invalid_configs(kw, status):
+    args = dict(tokens=64)
+    args.update(kw)
+    cfg = moe.make_dense_config(**args)
+    lib = moe.load_library()
+    assert lib.moe_dense_workspace_size(ctypes.byref(cfg)) == 0
+    st = lib.moe_dense_forward(ctypes.byref(cfg), *([None] * 6), 0, None)
+    assert st == status, moe.moe_last_error()
+
+
+def test_dense_errors_before_launch():
+    lib = moe.load_library()
+    cfg = moe.make_dense_config(64)
+    need = moe.moe_dense_workspace_size(cfg)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    st = lib.moe_dense_forward(ctypes.byref(cfg), fake, fake, None, fake, fake, fake, need, None)
+    assert st == moe.MOE_ERR_INVALID_ARG and "NULL" in moe.moe_last_error()
+    st = lib.moe_dense_forward(ctypes.byref(cfg), fake, fake, fake, fake, fake, fake, need - 1,
+                               None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    st = lib.moe_dense_forward(ctypes.byref(cfg), fake, fake, fake, fake, mis, fake, need, None)
+    assert st == moe.MOE_ERR_UNSUPPORTED
+    bad = moe.make_dense_config(64)
+    bad.reserved = 1
+    st = lib.moe_dense_forward(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, need, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
