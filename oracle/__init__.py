@@ -16,6 +16,12 @@ Parity status of each function (pins live in ``tests/test_oracle.py``):
            library matmul), scalar SwiGLU and clamp values.
   expert   pinned: scalar SwiGLU closed forms, dense MLP via library matmul.
   permute  pinned: agrees with a library stable argsort and with invariants.
+  e4m3_decode  pinned: all 256 codes against torch's float8_e4m3fn and the
+           format's named values (max 448, smallest normal 2^-6, smallest
+           subnormal 2^-9, NaN codes).
+  forward_fp8  pinned: with codes and scales that represent bf16 weights
+           exactly it equals forward on those weights; scales factor out of
+           each expert (scaling a row's scale scales that output unit).
   The reading "bias added after the sigmoid" and the reading of N(0, v) as a
   variance are not fixed by the pages' numbers: parity unpinned for those
   two readings (no page prints a worked routing example).
@@ -63,6 +69,9 @@ def _load():
         lib.oracle_forward.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp,
                                        vp, vp, ctypes.c_int]
         lib.oracle_expert.argtypes = [i32, i32, dbl, vp, i64, vp, vp, vp, vp, vp, ctypes.c_int]
+        lib.oracle_forward_fp8.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           i64, vp, vp, vp, ctypes.c_int]
+        lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
         lib.oracle_permute.argtypes = [i64, i32, i32, vp, vp, vp, vp]
         lib.oracle_hardware_threads.argtypes = []
         _lib = lib
@@ -141,6 +150,37 @@ def forward(cfg: Cfg, inp, tokens=None, forced_ids=None, threads=None):
     if rc:
         raise ValueError(f"oracle_forward failed ({rc})")
     return dict(y=y, ids=ids, w=w)
+
+
+def forward_fp8(cfg: Cfg, inp, fp8, tokens=None, threads=None):
+    """forward with the routed experts' weights from `fp8` (synth.Fp8Experts:
+    e4m3 codes and per-row scales); the shared expert from `inp`.
+    -> dict(y [n,H] f64, ids, w)."""
+    x = _c(inp.x, np.uint16)
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
+    n = cfg.T if tok is None else tok.size
+    y = np.empty((n, cfg.H), np.float64)
+    ids = np.empty((n, cfg.k), np.int32)
+    w = np.empty((n, cfg.k), np.float64)
+    args = [_c(inp.router_w, np.float32), _c(inp.router_b, np.float32),
+            _c(fp8.w8_gate, np.uint8), _c(fp8.w8_up, np.uint8), _c(fp8.w8_down, np.uint8),
+            _c(fp8.s_gate, np.float32), _c(fp8.s_up, np.float32), _c(fp8.s_down, np.float32),
+            _c(inp.ws_gate, np.uint16), _c(inp.ws_up, np.uint16), _c(inp.ws_down, np.uint16)]
+    rc = _load().oracle_forward_fp8(ctypes.byref(cfg), _p(x), *[_p(a) for a in args], _p(tok), n,
+                                    _p(y), _p(ids), _p(w), threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_forward_fp8 failed ({rc})")
+    return dict(y=y, ids=ids, w=w)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP e4m3 codes -> float64 values."""
+    c = _c(np.asarray(codes, np.uint8), np.uint8)
+    out = np.empty(c.shape, np.float64)
+    rc = _load().oracle_e4m3_decode(_p(c), c.size, _p(out))
+    if rc:
+        raise ValueError("oracle_e4m3_decode failed")
+    return out
 
 
 def expert(rows, gate, up, down, limit=0.0, threads=None):

@@ -74,32 +74,68 @@ double swiglu(double g, double u, double limit) {
   return g * sigmoid(g) * u;  // SiLU(g) * u
 }
 
+// OCP FP8 E4M3 ("e4m3fn") code -> value, from the format's definition:
+// bit 7 sign, bits 6..3 exponent with bias 7, bits 2..0 mantissa; exponent 0
+// holds the subnormals (mantissa/8) * 2^-6; all-ones exponent and mantissa
+// is NaN (no infinities).  The FP8 checkpoints of the model card ("Official
+// weights: BF16 (also FP8 ...)" in the sglang-jax issue's model configuration)
+// store weights this way with a scale per output row.
+double e4m3_to_double(uint8_t c) {
+  const int sign = c >> 7, ex = (c >> 3) & 15, man = c & 7;
+  double v;
+  if (ex == 15 && man == 7)
+    v = std::numeric_limits<double>::quiet_NaN();
+  else if (ex == 0)
+    v = std::ldexp(man / 8.0, -6);
+  else
+    v = std::ldexp(1.0 + man / 8.0, ex - 7);
+  return sign ? -v : v;
+}
+
+// Weight matrices [rows][cols] as the oracle reads them: bf16, or e4m3 codes
+// times a per-row scale.
+struct Bf16W {
+  const uint16_t* p;
+  int64_t cols;
+  double operator()(int64_t r, int64_t c) const { return bf16_to_double(p[r * cols + c]); }
+};
+struct Fp8W {
+  const uint8_t* p;
+  const float* scale;
+  int64_t cols;
+  double operator()(int64_t r, int64_t c) const {
+    return e4m3_to_double(p[r * cols + c]) * static_cast<double>(scale[r]);
+  }
+};
+
 // One SwiGLU expert on one activation row: out[d] = sum_i down[d][i] * a[i],
 // a[i] = swiglu(gate[i] . x, up[i] . x).  Optionally returns a (the
 // intermediate) in h.
-void expert_row(const double* x, int H, int I, const uint16_t* gate, const uint16_t* up,
-                const uint16_t* down, double limit, double* out, double* h) {
+template <class W>
+void expert_row_w(const double* x, int H, int I, const W& gate, const W& up, const W& down,
+                  double limit, double* out, double* h) {
   std::vector<double> a(I);
   for (int i = 0; i < I; ++i) {
     double g = 0.0, u = 0.0;
-    const uint16_t* gr = gate + static_cast<int64_t>(i) * H;
-    const uint16_t* ur = up + static_cast<int64_t>(i) * H;
     for (int c = 0; c < H; ++c) {
-      g += x[c] * bf16_to_double(gr[c]);
-      u += x[c] * bf16_to_double(ur[c]);
+      g += x[c] * gate(i, c);
+      u += x[c] * up(i, c);
     }
     a[i] = swiglu(g, u, limit);
     if (h) h[i] = a[i];
   }
   for (int d = 0; d < H; ++d) {
-    const uint16_t* dr = down + static_cast<int64_t>(d) * I;
     double o = 0.0;
-    for (int i = 0; i < I; ++i) o += bf16_to_double(dr[i]) * a[i];
+    for (int i = 0; i < I; ++i) o += down(d, i) * a[i];
     out[d] = o;
   }
 }
 
-// Router of one token: sigmoid scores s[e] and selection keys s[e] + b[e].
+void expert_row(const double* x, int H, int I, const uint16_t* gate, const uint16_t* up,
+                const uint16_t* down, double limit, double* out, double* h) {
+  expert_row_w(x, H, I, Bf16W{gate, H}, Bf16W{up, H}, Bf16W{down, I}, limit, out, h);
+}
+
 void router_row(const Cfg& c, const double* x, const float* wg, const float* bias, double* s,
                 double* key) {
   for (int e = 0; e < c.E; ++e) {
@@ -224,6 +260,55 @@ int oracle_forward(const Cfg* c, const uint16_t* x, const float* wg, const float
     if (ids_out) std::copy(ids.begin(), ids.end(), ids_out + n * c->k);
     if (w_out) std::copy(w.begin(), w.end(), w_out + n * c->k);
   });
+  return 0;
+}
+
+// oracle_forward with the routed experts' weights in FP8: e4m3 codes
+// w8_gate/w8_up [E][I][H], w8_down [E][H][I] and fp32 scales per output row
+// s_gate/s_up [E][I], s_down [E][H]; weight = e4m3_to_double(code) * scale.
+// The shared expert stays bf16.
+int oracle_forward_fp8(const Cfg* c, const uint16_t* x, const float* wg, const float* bias,
+                       const uint8_t* w8_gate, const uint8_t* w8_up, const uint8_t* w8_down,
+                       const float* s_gate, const float* s_up, const float* s_down,
+                       const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
+                       const int64_t* tokens, int64_t ntok, double* y, int32_t* ids_out,
+                       double* w_out, int threads) {
+  if (!cfg_ok(c) || !x || !wg || !w8_gate || !w8_up || !w8_down || !s_gate || !s_up || !s_down ||
+      !y || ntok < 0)
+    return 1;
+  if (c->Is > 0 && (!ws_gate || !ws_up || !ws_down)) return 1;
+  const int64_t HI = static_cast<int64_t>(c->H) * c->I;
+  parallel_for(ntok, threads, [&](int64_t n) {
+    const int64_t t = tokens ? tokens[n] : n;
+    std::vector<double> xr(c->H), s(c->E), key(c->E), o(c->H), acc(c->H, 0.0), w(c->k);
+    std::vector<int32_t> ids(c->k);
+    for (int h = 0; h < c->H; ++h) xr[h] = bf16_to_double(x[t * c->H + h]);
+    router_row(*c, xr.data(), wg, bias, s.data(), key.data());
+    select_topk(*c, key.data(), ids.data());
+    gating_weights(*c, s.data(), ids.data(), w.data());
+    for (int j = 0; j < c->k; ++j) {
+      const int64_t e = ids[j];
+      expert_row_w(xr.data(), c->H, c->I, Fp8W{w8_gate + e * HI, s_gate + e * c->I, c->H},
+                   Fp8W{w8_up + e * HI, s_up + e * c->I, c->H},
+                   Fp8W{w8_down + e * HI, s_down + e * c->H, c->I}, c->limit, o.data(), nullptr);
+      for (int d = 0; d < c->H; ++d) acc[d] += w[j] * o[d];
+    }
+    if (c->Is > 0) {
+      expert_row(xr.data(), c->H, c->Is, ws_gate, ws_up, ws_down, c->limit_shared, o.data(),
+                 nullptr);
+      for (int d = 0; d < c->H; ++d) acc[d] += o[d];
+    }
+    std::copy(acc.begin(), acc.end(), y + n * c->H);
+    if (ids_out) std::copy(ids.begin(), ids.end(), ids_out + n * c->k);
+    if (w_out) std::copy(w.begin(), w.end(), w_out + n * c->k);
+  });
+  return 0;
+}
+
+// e4m3 codes -> values (for the format's pins).
+int oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
+  if (n < 0 || (n > 0 && (!codes || !out))) return 1;
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_to_double(codes[i]);
   return 0;
 }
 

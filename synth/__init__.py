@@ -57,6 +57,9 @@ def _load():
         lib.synth_choose.argtypes = [u64, u64, i32, i32, vp]
         lib.synth_words.argtypes = [u64, u64, vp, i64]
         lib.synth_words.restype = None
+        lib.synth_normal_e4m3_rows.argtypes = [u64, u64, dbl, dbl, vp, vp, i64, i64, ctypes.c_int]
+        lib.synth_e4m3_encode.argtypes = [vp, i64, vp]
+        lib.synth_e4m3_encode.restype = None
         lib.synth_splitmix64_next.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
         lib.synth_splitmix64_next.restype = ctypes.c_uint64
         _lib = lib
@@ -110,6 +113,24 @@ def words(seed, tensor, n) -> np.ndarray:
 def splitmix64_sequence(state: int, n: int) -> list[int]:
     s = ctypes.c_uint64(state)
     return [int(_load().synth_splitmix64_next(ctypes.byref(s))) for _ in range(n)]
+
+
+def normal_e4m3_rows(seed, tensor, rows, row_len, std, mean=0.0):
+    """rows x row_len normals (the stream normal_bf16 draws) stored as OCP
+    e4m3 codes with a per-row fp32 scale max|row| / 448."""
+    codes = np.empty((int(rows), int(row_len)), dtype=np.uint8)
+    scales = np.empty(int(rows), dtype=np.float32)
+    _load().synth_normal_e4m3_rows(seed, tensor, mean, std, codes.ctypes.data, scales.ctypes.data,
+                                   rows, row_len, threads())
+    return codes, scales
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """Codes of values with |v| <= 448 (round to nearest even), for tests."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().synth_e4m3_encode(v.ctypes.data, v.size, out.ctypes.data)
+    return out
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -215,6 +236,28 @@ def gen_experts(wl: Workload):
         su = np.zeros((0, H), np.uint16)
         sd = np.zeros((H, 0), np.uint16)
     return wg, wu, wd, sg, su, sd
+
+
+@dataclasses.dataclass
+class Fp8Experts:
+    """Routed-expert weights as OCP e4m3 codes with one fp32 scale per output
+    row (weight = decode(code) * scale): the same normal draws as
+    gen_experts, quantised row by row."""
+    w8_gate: np.ndarray    # [E][I][H] uint8
+    s_gate: np.ndarray     # [E][I] f32
+    w8_up: np.ndarray      # [E][I][H] uint8
+    s_up: np.ndarray       # [E][I] f32
+    w8_down: np.ndarray    # [E][H][I] uint8
+    s_down: np.ndarray     # [E][H] f32
+
+
+def gen_experts_fp8(wl: Workload) -> Fp8Experts:
+    E, I, H = wl.E, wl.I, wl.H
+    g, sg = normal_e4m3_rows(wl.seed, T_WGATE, E * I, H, math.sqrt(1.0 / H))
+    u, su = normal_e4m3_rows(wl.seed, T_WUP, E * I, H, math.sqrt(1.0 / H))
+    d, sd = normal_e4m3_rows(wl.seed, T_WDOWN, E * H, I, math.sqrt(1.0 / max(I, 1)))
+    return Fp8Experts(g.reshape(E, I, H), sg.reshape(E, I), u.reshape(E, I, H), su.reshape(E, I),
+                      d.reshape(E, H, I), sd.reshape(E, H))
 
 
 def make_inputs(wl: Workload, experts=None) -> Inputs:

@@ -191,3 +191,97 @@ uint64_t synth_splitmix64_next(uint64_t* state) {
   *state += GAMMA;
   return mix64(*state);
 }
+
+/* ------------------------------------------------------- fp8 (e4m3) rows */
+
+/* OCP FP8 E4M3 ("e4m3fn"): sign, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent 0 holds the subnormals m * 2^-9; 0x7F/0xFF are NaN, so the
+ * largest finite magnitude is 1.75 * 2^8 = 448.  Round to nearest, ties to
+ * even mantissa; |v| <= 448 is required (the caller scales rows so). */
+static uint8_t e4m3_rne(double v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  int ex;
+  frexp(a, &ex);                 /* a = f * 2^ex, f in [0.5, 1) */
+  int e = ex - 1;                /* a in [2^e, 2^(e+1)) */
+  int code;
+  if (e < -6) {
+    code = (int)nearbyint(ldexp(a, 9)); /* subnormal grid 2^-9; 8 is the smallest normal */
+  } else {
+    int m = (int)nearbyint((ldexp(a, -e) - 1.0) * 8.0);
+    if (m == 8) { m = 0; ++e; }
+    code = ((e + 7) << 3) | m;
+  }
+  if (code > 0x7E) code = 0x7E;  /* not reached for |v| <= 448 */
+  return (uint8_t)(sign | code);
+}
+
+typedef struct {
+  uint64_t base;
+  double mean, std;
+  int64_t row_begin, row_end, row_len;
+  uint8_t* codes;
+  float* scales;
+} rows_job_t;
+
+static void* run_rows(void* arg) {
+  rows_job_t* j = (rows_job_t*)arg;
+  float* row = (float*)malloc(sizeof(float) * (size_t)j->row_len);
+  if (!row) return NULL;
+  for (int64_t r = j->row_begin; r < j->row_end; ++r) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < j->row_len; ++i) {
+      const int64_t idx = r * j->row_len + i;
+      row[i] = (float)(j->mean + j->std * normal_at(j->base, (uint64_t)idx));
+      const float m = fabsf(row[i]);
+      if (m > amax) amax = m;
+    }
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    j->scales[r] = scale;
+    for (int64_t i = 0; i < j->row_len; ++i) {
+      double q = (double)row[i] / (double)scale;
+      if (q > 448.0) q = 448.0;
+      if (q < -448.0) q = -448.0;
+      j->codes[r * j->row_len + i] = e4m3_rne(q);
+    }
+  }
+  free(row);
+  return NULL;
+}
+
+/* rows x row_len weights drawn as synth_normal_bf16 draws them (same stream,
+ * same element index), stored as e4m3 codes with one fp32 scale per row:
+ * scale = max|row| / 448, code = e4m3(value / scale). */
+int synth_normal_e4m3_rows(uint64_t seed, uint64_t tensor, double mean, double std,
+                           uint8_t* codes, float* scales, int64_t rows, int64_t row_len,
+                           int threads) {
+  if (rows <= 0 || row_len <= 0) return 0;
+  if (threads < 1) threads = 1;
+  if (threads > 256) threads = 256;
+  if (rows < threads) threads = (int)rows;
+  pthread_t tid[256];
+  rows_job_t jobs[256];
+  const int64_t chunk = (rows + threads - 1) / threads;
+  int started = 0;
+  for (int t = 0; t < threads; ++t) {
+    rows_job_t j = {stream_base(seed, tensor), mean, std, (int64_t)t * chunk, 0, row_len, codes,
+                    scales};
+    j.row_end = j.row_begin + chunk < rows ? j.row_begin + chunk : rows;
+    if (j.row_begin >= j.row_end) break;
+    jobs[t] = j;
+    if (pthread_create(&tid[t], NULL, run_rows, &jobs[t]) != 0) {
+      run_rows(&jobs[t]);
+      tid[t] = 0;
+    }
+    started = t + 1;
+  }
+  for (int t = 0; t < started; ++t)
+    if (tid[t]) pthread_join(tid[t], NULL);
+  return 0;
+}
+
+/* The encoder alone, for tests: codes of n values (|v| <= 448). */
+void synth_e4m3_encode(const double* v, int64_t n, uint8_t* codes) {
+  for (int64_t i = 0; i < n; ++i) codes[i] = e4m3_rne(v[i]);
+}

@@ -336,3 +336,96 @@ def test_parameter_count_matches_pages():
     assert abs(active / 11e9 - 1) < 0.10
     # two matrices per expert instead of three would miss by a third
     assert abs((total - moe_layers * E * H * I) / 196e9 - 1) > 0.25
+
+
+# ------------------------------------------------------ FP8 (e4m3) weights
+
+def test_e4m3_decode_matches_library_and_named_values():
+    """OCP FP8 E4M3 (e4m3fn): every code against torch's float8_e4m3fn, and
+    the format's named values."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), codes[~same]
+    named = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x3C: 1.5, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in named.items():
+        assert got[c] == v, hex(c)
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.signbit(got[0x80]) and got[0x80] == 0.0
+    assert np.nanmax(np.abs(got)) == 448.0
+
+
+def test_synth_e4m3_encoder_matches_library():
+    """The input generator's encoder (round to nearest even) against torch's
+    conversion, over the normal and subnormal ranges."""
+    import torch
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 0.01, 20000),
+                        rng.uniform(-2 ** -6, 2 ** -6, 20000), [0.0, -0.0, 448.0, -448.0]])
+    v = v.astype(np.float32).astype(np.float64)  # values torch sees exactly
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(synth.e4m3_encode(v), ref)
+
+
+def _fp8_exact_case(seed):
+    """Experts whose e4m3-times-scale weights are exactly bf16 weights: random
+    codes of magnitude < 2^4 (no subnormals) and power-of-two scales per row."""
+    wl = TINY.with_(T=12)
+    inp = synth.make_inputs(wl)
+    rng = np.random.default_rng(seed)
+    E, I, H = wl.E, wl.I, wl.H
+
+    def codes(shape):
+        ex = rng.integers(1, 11, size=shape)           # exponent field 1..10: 2^-6 .. 2^3
+        man = rng.integers(0, 8, size=shape)
+        sign = rng.integers(0, 2, size=shape)
+        return ((sign << 7) | (ex << 3) | man).astype(np.uint8)
+
+    def scales(shape):
+        return np.ldexp(1.0, rng.integers(-12, -2, size=shape)).astype(np.float32)
+
+    fp8 = synth.Fp8Experts(codes((E, I, H)), scales((E, I)), codes((E, I, H)), scales((E, I)),
+                           codes((E, H, I)), scales((E, H)))
+
+    def as_bf16(c, s):
+        vals = oracle.e4m3_decode(c) * s[..., None].astype(np.float64)
+        return f32_to_bf16_bits(vals.astype(np.float32))
+
+    bf = dict(w_gate=as_bf16(fp8.w8_gate, fp8.s_gate), w_up=as_bf16(fp8.w8_up, fp8.s_up),
+              w_down=as_bf16(fp8.w8_down, fp8.s_down))
+    # bf16 holds these values exactly (8 significant bits >= e4m3's 4)
+    for name, c, s in (("w_gate", fp8.w8_gate, fp8.s_gate), ("w_down", fp8.w8_down, fp8.s_down)):
+        assert np.array_equal(bf16_bits_to_f32(bf[name]).astype(np.float64),
+                              oracle.e4m3_decode(c) * s[..., None])
+    return wl, inp, fp8, bf
+
+
+def test_fp8_forward_equals_bf16_forward_on_same_weights():
+    wl, inp, fp8, bf = _fp8_exact_case(11)
+    cfg = oracle.cfg_of(wl)
+    ref = oracle.forward(cfg, inp.__class__(**{**inp.__dict__, **bf}))
+    got = oracle.forward_fp8(cfg, inp, fp8)
+    assert np.array_equal(got["ids"], ref["ids"])
+    assert np.array_equal(got["y"], ref["y"])
+
+
+def test_fp8_row_scale_scales_one_output_unit():
+    """Doubling the scale of down row d of every expert doubles the routed
+    part of y[:, d] and leaves the other units alone (a scale per output row,
+    not per input column)."""
+    wl, inp, fp8, _ = _fp8_exact_case(12)
+    wl = wl.with_(Is=0)
+    inp = inp.__class__(**{**inp.__dict__, "ws_gate": None, "ws_up": None, "ws_down": None})
+    cfg = oracle.cfg_of(wl)
+    base = oracle.forward_fp8(cfg, inp, fp8)["y"]
+    d = 5
+    s2 = fp8.s_down.copy()
+    s2[:, d] *= 2
+    fp8b = synth.Fp8Experts(fp8.w8_gate, fp8.s_gate, fp8.w8_up, fp8.s_up, fp8.w8_down, s2)
+    got = oracle.forward_fp8(cfg, inp, fp8b)["y"]
+    assert np.array_equal(got[:, d], 2 * base[:, d])
+    others = np.arange(wl.H) != d
+    assert np.array_equal(got[:, others], base[:, others])
