@@ -277,6 +277,51 @@ def measure(wl, moe, synth, experts_host, copies, steps, warmup):
     return out, ids_h
 
 
+def measure_fp8(wl, moe, synth, copies8, shared, steps, warmup):
+    """moe_forward_fp8 (routed experts as e4m3 codes + row scales) on the
+    workload's inputs, the copies of the FP8 weights rotated per step."""
+    import numpy as np
+    import torch
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    x = dev(synth.gen_x(wl))
+    rw_h, rb_h, _ = synth.gen_router(wl)
+    rw, rb = dev(rw_h), (dev(rb_h) if wl.use_bias else None)
+    cfg = moe.make_config(wl.T, wl.H, wl.E, wl.k, wl.I, wl.Is, wl.routed_scaling,
+                          wl.renormalize, wl.limit, wl.limit_shared)
+    ws = moe.alloc_workspace(cfg)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        moe.moe_forward_fp8(cfg, x, rw, rb, *copies8[i % len(copies8)], *shared, y, ids, w, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    U = int(np.count_nonzero(np.bincount(ids.cpu().numpy().ravel(), minlength=wl.E)))
+    H, I, Is, T, E, P = wl.H, wl.I, wl.Is, wl.T, wl.E, wl.P
+    nbytes = U * (3.0 * H * I + 4.0 * (2 * I + H)) + 3.0 * H * Is * 2 + E * H * 4 + T * H * 2 * 2
+    flop = 2.0 * T * H * E + 6.0 * P * H * I + 6.0 * T * H * Is
+    t = ms * 1e-3
+    return dict(ms_per_step=round(ms, 5), tokens_per_s=round(T / t, 1),
+                gbs=round(nbytes / t * 1e-9, 1), frac_hbm=round(nbytes / t * 1e-9 / HBM_PEAK_GBS, 4),
+                tflops=round(flop / t * 1e-12, 2),
+                frac_mfma=round(flop / t * 1e-12 / BF16_PEAK_TFLOPS, 4), experts_used=U,
+                algorithmic_bytes=nbytes)
+
+
 def measure_dense(wl, moe, synth, steps, warmup):
     """The dense SwiGLU FFN (moe_dense_forward) on its workload: ms/step and
     the MFMA rate of its 6*T*H*I FLOPs."""
@@ -423,6 +468,27 @@ def main():
             experts_used=sres["experts_used"], stage_ms=sres["stage_ms"])
         log(f"[bench] step3: {sres['ms_per_step']:.4f} ms/step")
         del s_dev
+        torch.cuda.empty_cache()
+        # FP8 (e4m3) routed-expert weights on the decode and prefill workloads
+        log("[bench] fp8 experts: decode and prefill")
+        f8 = synth.gen_experts_fp8(wl)
+
+        def dev8(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+        c8 = [tuple(dev8(a) for a in (f8.w8_gate, f8.w8_up, f8.w8_down, f8.s_gate, f8.s_up,
+                                      f8.s_down))]
+        for _ in range(ncopy - 1):
+            c8.append(tuple(t.clone() for t in c8[0]))
+        del f8
+        shared = tuple(copies[0][3:6])
+        rec["workloads"]["decode_fp8"] = measure_fp8(wl, moe, synth, c8, shared, args.steps,
+                                                     args.warmup)
+        log(f"[bench] decode fp8: {rec['workloads']['decode_fp8']['ms_per_step']:.4f} ms/step")
+        rec["workloads"]["prefill_fp8"] = measure_fp8(synth.WORKLOADS["prefill"], moe, synth,
+                                                      c8[:2], shared, 10, 3)
+        log(f"[bench] prefill fp8: {rec['workloads']['prefill_fp8']['ms_per_step']:.4f} ms/step")
+        del c8
         torch.cuda.empty_cache()
         dw = synth.WORKLOADS["dense"]
         log(f"[bench] dense FFN T={dw.T} I={dw.Is}")

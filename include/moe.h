@@ -154,6 +154,25 @@ moe_status moe_forward_timed(const moe_config* cfg, const uint16_t* x, const flo
                              float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream,
                              hipEvent_t* events, int n_events);
 
+/* moe_forward with the routed experts' weights in FP8: the model card lists
+ * FP8 among the official weight formats (sglang-jax issue, "Model
+ * configuration": "Official weights: BF16 (also FP8 / ...)").  Each routed
+ * weight is decode(code) * scale of its output row, code an OCP FP8 E4M3
+ * ("e4m3fn": bias 7, no infinities, max 448) byte:
+ *   w8_gate, w8_up  [E][I][H] uint8 codes;  scale_gate, scale_up  [E][I] fp32
+ *   w8_down         [E][H][I] uint8 codes;  scale_down            [E][H] fp32
+ * The shared expert stays bf16 (ws_gate/ws_up/ws_down as in moe_forward).
+ * Products are formed exactly (every e4m3 value is a bf16 value) and
+ * accumulated in fp32; the row scale multiplies each accumulated sum.  Same
+ * workspace size, conventions and limits as moe_forward. */
+moe_status moe_forward_fp8(const moe_config* cfg, const uint16_t* x, const float* router_w,
+                           const float* router_bias, const uint8_t* w8_gate, const uint8_t* w8_up,
+                           const uint8_t* w8_down, const float* scale_gate,
+                           const float* scale_up, const float* scale_down,
+                           const uint16_t* ws_gate, const uint16_t* ws_up,
+                           const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
+                           float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Where an intermediate of moe_forward lives inside the workspace, for
  * inspection after the stream has finished (tests, debugging).  Writes the
  * byte offset and size; returns MOE_ERR_INVALID_ARG for an unknown id. */

@@ -78,12 +78,14 @@ def load_library():
     lib.moe_forward.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_forward_timed.argtypes = lib.moe_forward.argtypes + [ctypes.POINTER(vp), ctypes.c_int]
     lib.moe_workspace_view.argtypes = [cp, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.moe_forward_fp8.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, sz, vp]
     dp = ctypes.POINTER(moe_dense_config)
     lib.moe_dense_workspace_size.argtypes = [dp]
     lib.moe_dense_workspace_size.restype = sz
     lib.moe_dense_forward.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     for f in ("moe_route", "moe_permute", "moe_forward", "moe_forward_timed",
-              "moe_workspace_view", "moe_dense_forward"):
+              "moe_workspace_view", "moe_dense_forward", "moe_forward_fp8"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -91,7 +93,7 @@ def load_library():
 
 EXPORTED = ("moe_workspace_size", "moe_last_error", "moe_route", "moe_permute", "moe_forward",
             "moe_forward_timed", "moe_workspace_view", "moe_dense_workspace_size",
-            "moe_dense_forward")
+            "moe_dense_forward", "moe_forward_fp8")
 
 
 # ------------------------------------------------------------------ helpers
@@ -281,3 +283,26 @@ def moe_dense_forward(cfg, x, w_gate, w_up, w_down, y, ws, stream=None):
                                  _ptr(y, _bf16(), "y", cfg.tokens == 0),
                                  _ptr(ws, None, "ws"), ws.numel() * ws.element_size(),
                                  _stream(stream)))
+
+
+# ------------------------------------------------------------------ FP8 experts
+
+def _u8():
+    return (_torch().uint8, _torch().float8_e4m3fn)
+
+
+def moe_forward_fp8(cfg, x, router_w, router_bias, w8_gate, w8_up, w8_down, scale_gate, scale_up,
+                    scale_down, ws_gate, ws_up, ws_down, y, topk_ids_out, topk_w_out, ws,
+                    stream=None):
+    lib = load_library()
+    empty = cfg.tokens == 0
+    _check(lib.moe_forward_fp8(
+        ctypes.byref(cfg), _ptr(x, _bf16(), "x", empty), _ptr(router_w, _f32(), "router_w"),
+        _ptr(router_bias, _f32(), "router_bias", True), _ptr(w8_gate, _u8(), "w8_gate"),
+        _ptr(w8_up, _u8(), "w8_up"), _ptr(w8_down, _u8(), "w8_down"),
+        _ptr(scale_gate, _f32(), "scale_gate"), _ptr(scale_up, _f32(), "scale_up"),
+        _ptr(scale_down, _f32(), "scale_down"), _ptr(ws_gate, _bf16(), "ws_gate", True),
+        _ptr(ws_up, _bf16(), "ws_up", True), _ptr(ws_down, _bf16(), "ws_down", True),
+        _ptr(y, _bf16(), "y", empty), _ptr(topk_ids_out, _i32(), "topk_ids_out", True),
+        _ptr(topk_w_out, _f32(), "topk_w_out", True), _ptr(ws, None, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)))

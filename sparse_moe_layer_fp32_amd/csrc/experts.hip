@@ -73,22 +73,26 @@ __device__ __forceinline__ TileCoord tile_of(int u, int ntiles, int NT) {
   return {first + within % gm, within / gm};
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int S>
+template <int BM, int BN, int BK, int WM, int WN, int S, int WF = 0>
 struct Cfg {
   static constexpr int NW = WM * WN;
   static constexpr int THREADS = 64 * NW;
   static constexpr int MB = BM / WM / 32;     // 32-row blocks per wave
   static constexpr int NB = BN / WN / 32;     // 32-col blocks per wave
-  static constexpr int CH = BK / 8;           // 16-byte chunks per tile row
-  static constexpr int ROWB = BK * 2;         // bytes per tile row
-  static constexpr int RPI = 64 / CH;         // rows filled by one DMA instruction
+  static constexpr int CH = BK / 8;           // 16-byte chunks per A row (bf16)
+  static constexpr int ROWB = BK * 2;         // bytes per A row
+  static constexpr int RPI = 64 / CH;         // A rows filled by one DMA instruction
+  static constexpr int BROWB = WF ? BK : BK * 2;  // bytes per B row (e4m3 or bf16)
+  static constexpr int CHB = BROWB / 16;      // 16-byte chunks per B row
+  static constexpr int RPIB = 64 / CHB;       // B rows filled by one DMA instruction
   static constexpr int JA = BM / RPI / NW;    // A DMA instructions per wave per stage
-  static constexpr int JB = BN / RPI / NW;    // B DMA instructions per wave per stage
+  static constexpr int JB = BN / RPIB / NW;   // B DMA instructions per wave per stage
   static constexpr int NI = JA + JB;
   static constexpr int KS = BK / 16;          // MFMA k-substeps per stage
-  static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  static constexpr int STAGE_BYTES = BM * ROWB + BN * BROWB;
   static constexpr int LDS_BYTES = S * STAGE_BYTES;
   static_assert(CH == 4 || CH == 8, "k step of 32 or 64");
+  static_assert(CHB == 2 || CHB == 4 || CHB == 8, "B row of 32, 64 or 128 bytes");
   static_assert(MB >= 1 && NB >= 1 && JA >= 1 && JB >= 1, "tile shape");
   static_assert(NI * (S > 2 ? S - 2 : 1) <= 63, "vmcnt budget");
   // XOR swizzle of a row's 16-byte chunks.  The LDS serves 16 lanes (256
@@ -101,13 +105,26 @@ struct Cfg {
   static __device__ __forceinline__ int swz(int row) {
     return CH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
   }
+  // B rows: as above for bf16.  e4m3 fragments are 8-byte reads of 64- or
+  // 32-byte rows (32 lanes per cycle); the swizzle spreads the rows that
+  // share a bank window over the chunk slots (at most two lanes per bank).
+  static __device__ __forceinline__ int swzb(int row) {
+    return CHB == 8 ? ((row >> 1) & 7) : CHB == 4 ? ((row >> 2) & 3) : ((row >> 3) & 1);
+  }
 };
 
 // MODE 0: gate/up (+ SwiGLU), MODE 1: down (+ gating weight), MODE 2: the
 // router's logits as one dense GEMM over the bf16 planes of its weight.
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
+//
+// WF = 1: the routed experts' weights are e4m3 codes (B operand): DMA'd as
+// bytes, widened to bf16 exactly after the LDS read, and multiplied by their
+// row's scale in the epilogue (a scale per output row factors out of the
+// dot product).  Such launches carry no shared-expert tiles.
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0>
 __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
-  using C = Cfg<BM, BN, BK, WM, WN, S>;
+  using C = Cfg<BM, BN, BK, WM, WN, S, WF>;
+  using BT = typename std::conditional<WF == 1, uint8_t, uint16_t>::type;
+  static_assert(WF == 0 || MODE < 2, "e4m3 weights are for the expert GEMMs");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int ntiles = MODE == 2 ? static_cast<int>((a.T + BM - 1) / BM) : *a.ntiles;
@@ -124,6 +141,7 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     row0 = tile.y;
   }
   const bool shared = MODE != 2 && e == a.E;
+  if (WF == 1 && shared) return;  // shared tiles run in a bf16 launch
   const int H = a.H;
 
   // Problem shape of this group.
@@ -174,12 +192,23 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   }
   // B rows: each wave's rows are consecutive and lie in one matrix (for
   // gate/up the first half of the tile is W_gate, the second W_up).
-  const uint16_t* bmat;
+  const BT* bmat;
   uint32_t boff[C::JB];  // element offsets inside that matrix
   {
-    const int r0 = C::RPI * wid * C::JB;  // first B row of this wave
+    const int lrow_b = lane / C::CHB, pchunk_b = lane % C::CHB;
+    const int r0 = C::RPIB * wid * C::JB;  // first B row of this wave
     int mrow;
-    if (MODE == 0) {
+    if constexpr (WF == 1) {
+      const int64_t eo = static_cast<int64_t>(e) * a.I * H;
+      if (MODE == 0) {
+        const bool up = r0 >= BN / 2;
+        bmat = (up ? a.w8_up : a.w8_gate) + eo;
+        mrow = n0 + r0 - (up ? BN / 2 : 0);
+      } else {
+        bmat = a.w8_down + eo;
+        mrow = n0 + r0;
+      }
+    } else if (MODE == 0) {
       const bool up = r0 >= BN / 2;
       bmat = up ? (shared ? a.ws_up : a.w_up + static_cast<int64_t>(e) * a.I * H)
                 : (shared ? a.ws_gate : a.w_gate + static_cast<int64_t>(e) * a.I * H);
@@ -193,8 +222,9 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < C::JB; ++j) {
-      const int lchunk = pchunk ^ C::swz(r0 + C::RPI * j + lrow);
-      boff[j] = static_cast<uint32_t>((mrow + C::RPI * j + lrow) * K + lchunk * 8);
+      const int lchunk = pchunk_b ^ C::swzb(r0 + C::RPIB * j + lrow_b);
+      boff[j] = static_cast<uint32_t>((mrow + C::RPIB * j + lrow_b) * K +
+                                      lchunk * (16 / static_cast<int>(sizeof(BT))));
     }
   }
 
@@ -230,7 +260,7 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     } else {
       brow = wn * (BN / WN) + 32 * nb;
     }
-    b_off[nb] = BM * C::ROWB + (brow + fr) * C::ROWB;
+    b_off[nb] = BM * C::ROWB + (brow + fr) * C::BROWB;
   }
 
   const int KT = K / BK;
@@ -251,12 +281,25 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f32x16{};
 
   bf16x8 af[2][C::MB], bf[2][C::NB];
+  const int fswzb = C::swzb(fr);
   auto load_frags = [&](int kt, int ks, int set) {
     const uint8_t* st = smem + (kt % S) * C::STAGE_BYTES;
     const int sw = ((2 * ks + fh) ^ fswz) * 16;
+    if constexpr (WF == 1) {
+      // Logical chunk ks of the e4m3 row holds the 16 codes of k-substep ks;
+      // this lane's 8 are half fh.  The whole chunk is read (a single 16-byte
+      // LDS read, like the bf16 fragments) and the half selected in registers.
+      const int swb = (ks ^ fswzb) * 16;
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-      bf[set][nb] = *reinterpret_cast<const bf16x8*>(st + b_off[nb] + sw);
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(st + b_off[nb] + swb);
+        bf[set][nb] = fh ? e4m3x8_to_bf16(raw[2], raw[3]) : e4m3x8_to_bf16(raw[0], raw[1]);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+        bf[set][nb] = *reinterpret_cast<const bf16x8*>(st + b_off[nb] + sw);
+    }
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
       af[set][mb] = *reinterpret_cast<const bf16x8*>(st + a_off[mb] + sw);
@@ -385,25 +428,35 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
       if (s < KT)
 #pragma unroll
         for (int d = 0; d < C::NI; ++d) issue_one(s, d);
-    for (int kt = 0; kt < KT; ++kt) {
+    auto wait_stage = [&](int kt) {
       if (kt + S - 2 < KT)
         wait_vmcnt<(S - 2) * C::NI>();
       else
         wait_vmcnt<0>();
       barrier();
-      const bool refill = kt + S - 1 < KT;
-      if (!has_rows) {
-        if (refill)
+    };
+    if (!has_rows) {
+      // Waves without rows keep the same DMA and barrier sequence (a loop of
+      // its own: a branch around the MFMAs would move the accumulators).
+      for (int kt = 0; kt < KT; ++kt) {
+        wait_stage(kt);
+        if (kt + S - 1 < KT)
           for (int d = 0; d < C::NI; ++d) issue_one(kt + S - 1, d);
-        continue;
       }
+      return;
+    }
+    // REFILL is a compile-time flag: a runtime branch between the MFMAs
+    // would move the accumulators between register files every step.
+    auto step = [&](int kt, auto REFILL) {
+      constexpr bool refill = decltype(REFILL)::value;
+      wait_stage(kt);
       load_frags(kt, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         if (ks + 1 < C::KS) load_frags(kt, ks + 1, (ks + 1) & 1);
         mfmas(ks & 1, [&](int i) {
           const int g = ks * C::MB * C::NB + i;  // MFMA index in the stage
-          if (g % DMA_EVERY == DMA_EVERY - 1 && g / DMA_EVERY < C::NI && refill)
+          if (refill && g % DMA_EVERY == DMA_EVERY - 1 && g / DMA_EVERY < C::NI)
             issue_one(kt + S - 1, g / DMA_EVERY);
         });
         __builtin_amdgcn_sched_barrier(0);
@@ -411,7 +464,10 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
       if (refill && MFMAS / DMA_EVERY < C::NI)  // more DMAs than MFMA slots
 #pragma unroll
         for (int d = MFMAS / DMA_EVERY; d < C::NI; ++d) issue_one(kt + S - 1, d);
-    }
+    };
+    int kt = 0;
+    for (; kt + S - 1 < KT; ++kt) step(kt, std::true_type{});
+    for (; kt < KT; ++kt) step(kt, std::false_type{});
   }
   if (!has_rows) return;
 
@@ -425,6 +481,19 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     uint16_t* out = shared ? a.h_shared : a.h_routed;
     const float lim = shared ? a.limit_shared : a.limit;
     const int half = C::NB / 2;
+    // e4m3 weights: the scales of this lane's gate and up output rows
+    f32x4 sg[C::NB / 2][4], su[C::NB / 2][4];
+    if constexpr (WF == 1) {
+      const float* sgp = a.s_gate + static_cast<int64_t>(e) * a.I + n0 + wn * (BN / 2 / WN) + 4 * fh;
+      const float* sup = a.s_up + static_cast<int64_t>(e) * a.I + n0 + wn * (BN / 2 / WN) + 4 * fh;
+#pragma unroll
+      for (int nb = 0; nb < half; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          sg[nb][g] = *reinterpret_cast<const f32x4*>(sgp + 32 * nb + 8 * g);
+          su[nb][g] = *reinterpret_cast<const f32x4*>(sup + 32 * nb + 8 * g);
+        }
+    }
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
       if (row + 32 * mb >= rows) continue;
@@ -436,8 +505,14 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
         for (int g = 0; g < 4; ++g) {
           float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            hv[q] = swiglu_f32(acc[mb][nb][4 * g + q], acc[mb][nb + half][4 * g + q], lim);
+          for (int q = 0; q < 4; ++q) {
+            float gv = acc[mb][nb][4 * g + q], uv = acc[mb][nb + half][4 * g + q];
+            if constexpr (WF == 1) {
+              gv *= sg[nb][g][q];
+              uv *= su[nb][g][q];
+            }
+            hv[q] = swiglu_f32(gv, uv, lim);
+          }
           *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * g) =
               make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
@@ -459,6 +534,15 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
     }
   } else {
     uint16_t* out = shared ? a.o_shared : a.o_routed;
+    // e4m3 weights: the scales of this lane's output rows (columns of o)
+    f32x4 sd[C::NB][4];
+    if constexpr (WF == 1) {
+      const float* sdp = a.s_down + static_cast<int64_t>(e) * H + n0 + wn * (BN / WN) + 4 * fh;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) sd[nb][g] = *reinterpret_cast<const f32x4*>(sdp + 32 * nb + 8 * g);
+    }
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
       if (row + 32 * mb >= rows) continue;
@@ -469,9 +553,14 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x16& v = acc[mb][nb];
+          float o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            o[q] = v[4 * g + q] * wt[mb];
+            if constexpr (WF == 1) o[q] *= sd[nb][g][q];
+          }
           *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * g) =
-              make_uint2(pack_bf16x2(v[4 * g] * wt[mb], v[4 * g + 1] * wt[mb]),
-                         pack_bf16x2(v[4 * g + 2] * wt[mb], v[4 * g + 3] * wt[mb]));
+              make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
     }
   }
@@ -527,15 +616,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   *reinterpret_cast<u32x4*>(y + t * H + d) = outv;
 }
 
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0>
 hipError_t launch_one(const ExpertArgs& a, int tile_capacity, int NT, hipStream_t stream) {
-  using C = Cfg<BM, BN, BK, WM, WN, S>;
+  using C = Cfg<BM, BN, BK, WM, WN, S, WF>;
   const int64_t units = static_cast<int64_t>(tile_capacity) * NT;
   const int64_t grid = (units + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid <= 0) return hipSuccess;
   ExpertArgs b = a;
   b.NT = NT;
-  expert_gemm<MODE, BM, BN, BK, WM, WN, S>
+  expert_gemm<MODE, BM, BN, BK, WM, WN, S, WF>
       <<<static_cast<unsigned>(grid), C::THREADS, 0, stream>>>(b);
   return hipGetLastError();
 }
@@ -564,14 +653,26 @@ int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape) {
 // flight, 8 waves of 128 x 64 (two per SIMD, so one wave's stalls are
 // covered by the other's MFMAs); small = 64 x 128, k step 64, 3-deep ring,
 // 4 waves, two blocks per CU.
-hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream) {
+hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream,
+                         int fp8) {
   const int maxn = std::max(a.I, a.Is);
+  if (fp8) {
+    if (shape == kTileBig)
+      return launch_one<0, 256, 256, 32, 2, 4, 4, 1>(a, tile_capacity, (a.I + 127) / 128, stream);
+    return launch_one<0, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, (a.I + 63) / 64, stream);
+  }
   if (shape == kTileBig)
     return launch_one<0, 256, 256, 32, 2, 4, 4>(a, tile_capacity, (maxn + 127) / 128, stream);
   return launch_one<0, 64, 128, 64, 2, 2, 3>(a, tile_capacity, (maxn + 63) / 64, stream);
 }
 
-hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream) {
+hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream,
+                       int fp8) {
+  if (fp8) {
+    if (shape == kTileBig)
+      return launch_one<1, 256, 256, 32, 2, 4, 4, 1>(a, tile_capacity, a.H / 256, stream);
+    return launch_one<1, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, a.H / 128, stream);
+  }
   if (shape == kTileBig)
     return launch_one<1, 256, 256, 32, 2, 4, 4>(a, tile_capacity, a.H / 256, stream);
   return launch_one<1, 64, 128, 64, 2, 2, 3>(a, tile_capacity, a.H / 128, stream);

@@ -35,6 +35,14 @@ struct ExpertArgs {
   uint16_t* o_routed;       // [P][H]
   uint16_t* o_shared;       // [T][H]
   int NT;                   // column tiles (set by the launcher)
+  // FP8 routed experts (when the launch says so): e4m3 codes in the layouts of
+  // w_gate/w_up/w_down and one fp32 scale per output row.
+  const uint8_t* w8_gate;   // [E][I][H]
+  const uint8_t* w8_up;     // [E][I][H]
+  const uint8_t* w8_down;   // [E][H][I]
+  const float* s_gate;      // [E][I]
+  const float* s_up;        // [E][I]
+  const float* s_down;      // [E][H]
   // Router logits as a GEMM (mode 2): zout[t][n] = x[t] . wsplit[n], n < Np.
   const uint16_t* wsplit;   // [Np][H] bf16 planes of the router weight, row 3e+p
   float* zout;              // [T][Np]
@@ -76,8 +84,10 @@ int permute_hist_stride(int P);  // histogram row stride: chunk count rounded up
 int experts_pick_shape(int64_t T, int P, int E, int H, int I, int Is);
 int experts_tile_rows(int shape);
 int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape);
-hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream);
-hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream);
+hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream,
+                         int fp8 = 0);
+hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream,
+                       int fp8 = 0);
 hipError_t launch_combine(const uint16_t* o_routed, const uint16_t* o_shared,
                           const int32_t* pair_pos, int k, int64_t T, int H, uint16_t* y,
                           hipStream_t stream);

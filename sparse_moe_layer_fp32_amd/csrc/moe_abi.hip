@@ -42,7 +42,9 @@ struct Plan {
   int C;         // permutation chunks, padded to a multiple of 4
   int shape;     // expert GEMM tile shape (kTileBig / kTileSmall)
   int tile_cap;  // capacity of the GEMM tile list
-  size_t zpart, wsplit, ids, w, rank, hist, base, offsets, sorted, pos, wsorted, tiles, ntiles, h, o, total;
+  size_t zpart, wsplit, ids, w, rank, hist, base, offsets, sorted, pos, wsorted, tiles, ntiles,
+      stiles, nstiles, h, o, total;
+  int stile_cap;  // tiles of the shared expert alone (FP8 path)
 };
 
 moe_status validate(const moe_config* c) {
@@ -107,6 +109,10 @@ void make_plan(const moe_config* c, Plan* p) {
   p->wsorted = take(P * 4);
   p->tiles = take(static_cast<size_t>(p->tile_cap) * 8);
   p->ntiles = take(16);
+  const int bm = moe::experts_tile_rows(p->shape);
+  p->stile_cap = static_cast<int>(std::max<int64_t>(1, (p->T + bm - 1) / bm));
+  p->stiles = take(static_cast<size_t>(p->stile_cap) * 8);
+  p->nstiles = take(16);
   p->h = take((P * p->I + T64 * p->Is) * 2);
   p->o = take((P + (p->Is > 0 ? T64 : 0)) * p->H * 2);
   p->total = off;
@@ -169,10 +175,10 @@ moe_status route_impl(const Plan& p, const moe_config* c, const uint16_t* x, con
 // in the workspace for the down GEMM's epilogue.
 moe_status permute_impl(const Plan& p, const int32_t* ids, int32_t* offsets, int32_t* sorted,
                         int32_t* pos, const float* w, void* ws, hipStream_t stream,
-                        hipEvent_t* ev) {
+                        hipEvent_t* ev, bool shared_tiles = true) {
   MOE_CHECK_LAUNCH(
       moe::launch_permute(ids, static_cast<int>(p.P), p.E, p.T, moe::experts_tile_rows(p.shape),
-                          p.Is > 0, at<int32_t>(ws, p.rank), at<int32_t>(ws, p.hist),
+                          shared_tiles && p.Is > 0, at<int32_t>(ws, p.rank), at<int32_t>(ws, p.hist),
                           at<int32_t>(ws, p.base), offsets, sorted, pos, at<int2>(ws, p.tiles),
                           at<int32_t>(ws, p.ntiles), w, w ? at<float>(ws, p.wsorted) : nullptr,
                           stream, ev),
@@ -180,20 +186,32 @@ moe_status permute_impl(const Plan& p, const int32_t* ids, int32_t* offsets, int
   return MOE_OK;
 }
 
+// Routed-expert weights as e4m3 codes with per-output-row scales.
+struct Fp8Weights {
+  const uint8_t *gate, *up, *down;
+  const float *s_gate, *s_up, *s_down;
+};
+
 moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* router_w,
                         const float* router_bias, const uint16_t* w_gate, const uint16_t* w_up,
                         const uint16_t* w_down, const uint16_t* ws_gate, const uint16_t* ws_up,
                         const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
                         float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                        hipEvent_t* ev) {
+                        hipEvent_t* ev, const Fp8Weights* f8 = nullptr) {
   moe_status st = validate(c);
   if (st) return st;
-  if (!router_w || !w_gate || !w_up || !w_down || (c->tokens > 0 && (!x || !y)))
+  const bool routed_ok = f8 ? (f8->gate && f8->up && f8->down && f8->s_gate && f8->s_up &&
+                               f8->s_down)
+                            : (w_gate && w_up && w_down);
+  if (!router_w || !routed_ok || (c->tokens > 0 && (!x || !y)))
     return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
   if (c->inter_shared > 0 && (!ws_gate || !ws_up || !ws_down))
     return fail(MOE_ERR_INVALID_ARG, "inter_shared > 0 but a shared-expert weight is NULL");
   const void* ptrs[] = {x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                        y, topk_ids_out, topk_w_out};
+                        y, topk_ids_out, topk_w_out,
+                        f8 ? f8->gate : nullptr, f8 ? f8->up : nullptr, f8 ? f8->down : nullptr,
+                        f8 ? f8->s_gate : nullptr, f8 ? f8->s_up : nullptr,
+                        f8 ? f8->s_down : nullptr};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(MOE_ERR_UNSUPPORTED, "pointer %p not 16-byte aligned", q);
   Plan p;
@@ -212,7 +230,8 @@ moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* rou
   uint16_t* o_shared = p.Is > 0 ? o_routed + static_cast<size_t>(p.P) * p.H : nullptr;
 
   if ((st = route_impl(p, c, x, router_w, router_bias, ids, w, ws, stream, ev))) return st;
-  if ((st = permute_impl(p, ids, offsets, sorted, pos, w, ws, stream, ev ? ev + 2 : nullptr)))
+  if ((st = permute_impl(p, ids, offsets, sorted, pos, w, ws, stream, ev ? ev + 2 : nullptr,
+                         !f8)))
     return st;
 
   moe::ExpertArgs g{};
@@ -240,10 +259,32 @@ moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* rou
   g.h_shared = h_shared;
   g.o_routed = o_routed;
   g.o_shared = o_shared;
+  if (f8) {
+    g.w8_gate = f8->gate;
+    g.w8_up = f8->up;
+    g.w8_down = f8->down;
+    g.s_gate = f8->s_gate;
+    g.s_up = f8->s_up;
+    g.s_down = f8->s_down;
+  }
+  // FP8: routed tiles run the e4m3 kernels; the shared expert (bf16) runs
+  // from a tile list of its own.
+  moe::ExpertArgs gs = g;
+  if (f8 && p.Is > 0) {
+    gs.tiles = at<int2>(ws, p.stiles);
+    gs.ntiles = at<int32_t>(ws, p.nstiles);
+    MOE_CHECK_LAUNCH(moe::launch_dense_tiles(at<int2>(ws, p.stiles), at<int32_t>(ws, p.nstiles),
+                                             p.T, moe::experts_tile_rows(p.shape), p.E, stream),
+                     "shared tile list");
+  }
   if (ev) hipEventRecord(ev[5], stream);
-  MOE_CHECK_LAUNCH(moe::launch_gateup(g, p.shape, p.tile_cap, stream), "gate/up gemm");
+  MOE_CHECK_LAUNCH(moe::launch_gateup(g, p.shape, p.tile_cap, stream, f8 ? 1 : 0), "gate/up gemm");
+  if (f8 && p.Is > 0)
+    MOE_CHECK_LAUNCH(moe::launch_gateup(gs, p.shape, p.stile_cap, stream, 0), "shared gate/up");
   if (ev) hipEventRecord(ev[6], stream);
-  MOE_CHECK_LAUNCH(moe::launch_down(g, p.shape, p.tile_cap, stream), "down gemm");
+  MOE_CHECK_LAUNCH(moe::launch_down(g, p.shape, p.tile_cap, stream, f8 ? 1 : 0), "down gemm");
+  if (f8 && p.Is > 0)
+    MOE_CHECK_LAUNCH(moe::launch_down(gs, p.shape, p.stile_cap, stream, 0), "shared down");
 
   if (ev) hipEventRecord(ev[7], stream);
   MOE_CHECK_LAUNCH(moe::launch_combine(o_routed, o_shared, pos, p.k, p.T, p.H, y, stream),
@@ -425,6 +466,18 @@ moe_status moe_forward_timed(const moe_config* cfg, const uint16_t* x, const flo
     if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "event %d is NULL", i);
   return forward_impl(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
                       y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, events);
+}
+
+moe_status moe_forward_fp8(const moe_config* cfg, const uint16_t* x, const float* router_w,
+                           const float* router_bias, const uint8_t* w8_gate, const uint8_t* w8_up,
+                           const uint8_t* w8_down, const float* scale_gate,
+                           const float* scale_up, const float* scale_down,
+                           const uint16_t* ws_gate, const uint16_t* ws_up,
+                           const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
+                           float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const Fp8Weights f8{w8_gate, w8_up, w8_down, scale_gate, scale_up, scale_down};
+  return forward_impl(cfg, x, router_w, router_bias, nullptr, nullptr, nullptr, ws_gate, ws_up,
+                      ws_down, y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, nullptr, &f8);
 }
 
 moe_status moe_workspace_view(const moe_config* cfg, int which, size_t* offset, size_t* bytes) {
