@@ -119,29 +119,15 @@ struct Cfg {
 // WF = 1: the routed experts' weights are e4m3 codes (B operand): DMA'd as
 // bytes, widened to bf16 exactly after the LDS read, and multiplied by their
 // row's scale in the epilogue (a scale per output row factors out of the
-// dot product).  Such launches carry no shared-expert tiles.
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0>
-__global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
+// dot product).  The shared expert's tiles (bf16 weights) in such a launch
+// take the bf16 body: the choice is made once per block.
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF>
+__device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, TileCoord tc,
+                                          int e, int row0) {
   using C = Cfg<BM, BN, BK, WM, WN, S, WF>;
   using BT = typename std::conditional<WF == 1, uint8_t, uint16_t>::type;
   static_assert(WF == 0 || MODE < 2, "e4m3 weights are for the expert GEMMs");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
-
-  const int ntiles = MODE == 2 ? static_cast<int>((a.T + BM - 1) / BM) : *a.ntiles;
-  const int u = xcd_remap(blockIdx.x, ntiles * a.NT);
-  if (u < 0) return;
-  const TileCoord tc = tile_of(u, ntiles, a.NT);
-  int e, row0;
-  if (MODE == 2) {
-    e = 0;
-    row0 = tc.mt * BM;
-  } else {
-    const int2 tile = a.tiles[tc.mt];
-    e = tile.x;
-    row0 = tile.y;
-  }
   const bool shared = MODE != 2 && e == a.E;
-  if (WF == 1 && shared) return;  // shared tiles run in a bf16 launch
   const int H = a.H;
 
   // Problem shape of this group.
@@ -566,6 +552,35 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   }
 }
 
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0>
+__global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
+  using C0 = Cfg<BM, BN, BK, WM, WN, S, 0>;
+  using C1 = Cfg<BM, BN, BK, WM, WN, S, WF>;
+  constexpr int LDS = C0::LDS_BYTES > C1::LDS_BYTES ? C0::LDS_BYTES : C1::LDS_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+
+  const int ntiles = MODE == 2 ? static_cast<int>((a.T + BM - 1) / BM) : *a.ntiles;
+  const int u = xcd_remap(blockIdx.x, ntiles * a.NT);
+  if (u < 0) return;
+  const TileCoord tc = tile_of(u, ntiles, a.NT);
+  int e, row0;
+  if (MODE == 2) {
+    e = 0;
+    row0 = tc.mt * BM;
+  } else {
+    const int2 tile = a.tiles[tc.mt];
+    e = tile.x;
+    row0 = tile.y;
+  }
+  if constexpr (WF == 1) {
+    if (e == a.E) {  // shared expert: bf16 weights
+      gemm_tile<MODE, BM, BN, BK, WM, WN, S, 0>(a, smem, tc, e, row0);
+      return;
+    }
+  }
+  gemm_tile<MODE, BM, BN, BK, WM, WN, S, WF>(a, smem, tc, e, row0);
+}
+
 // y[t] = o_shared[t] + sum_j o[pos(t, j)] in slot order j = 0..k-1, fp32,
 // rounded once to bf16.  One thread per 8 consecutive outputs.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o_routed,
@@ -658,8 +673,8 @@ hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipS
   const int maxn = std::max(a.I, a.Is);
   if (fp8) {
     if (shape == kTileBig)
-      return launch_one<0, 256, 256, 32, 2, 4, 4, 1>(a, tile_capacity, (a.I + 127) / 128, stream);
-    return launch_one<0, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, (a.I + 63) / 64, stream);
+      return launch_one<0, 256, 256, 32, 2, 4, 4, 1>(a, tile_capacity, (maxn + 127) / 128, stream);
+    return launch_one<0, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, (maxn + 63) / 64, stream);
   }
   if (shape == kTileBig)
     return launch_one<0, 256, 256, 32, 2, 4, 4>(a, tile_capacity, (maxn + 127) / 128, stream);

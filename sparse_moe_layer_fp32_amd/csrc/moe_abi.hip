@@ -42,9 +42,8 @@ struct Plan {
   int C;         // permutation chunks, padded to a multiple of 4
   int shape;     // expert GEMM tile shape (kTileBig / kTileSmall)
   int tile_cap;  // capacity of the GEMM tile list
-  size_t zpart, wsplit, ids, w, rank, hist, base, offsets, sorted, pos, wsorted, tiles, ntiles,
-      stiles, nstiles, h, o, total;
-  int stile_cap;  // tiles of the shared expert alone (FP8 path)
+  size_t zpart, wsplit, ids, w, rank, hist, base, offsets, sorted, pos, wsorted, tiles, ntiles, h,
+      o, total;
 };
 
 moe_status validate(const moe_config* c) {
@@ -109,10 +108,6 @@ void make_plan(const moe_config* c, Plan* p) {
   p->wsorted = take(P * 4);
   p->tiles = take(static_cast<size_t>(p->tile_cap) * 8);
   p->ntiles = take(16);
-  const int bm = moe::experts_tile_rows(p->shape);
-  p->stile_cap = static_cast<int>(std::max<int64_t>(1, (p->T + bm - 1) / bm));
-  p->stiles = take(static_cast<size_t>(p->stile_cap) * 8);
-  p->nstiles = take(16);
   p->h = take((P * p->I + T64 * p->Is) * 2);
   p->o = take((P + (p->Is > 0 ? T64 : 0)) * p->H * 2);
   p->total = off;
@@ -175,10 +170,10 @@ moe_status route_impl(const Plan& p, const moe_config* c, const uint16_t* x, con
 // in the workspace for the down GEMM's epilogue.
 moe_status permute_impl(const Plan& p, const int32_t* ids, int32_t* offsets, int32_t* sorted,
                         int32_t* pos, const float* w, void* ws, hipStream_t stream,
-                        hipEvent_t* ev, bool shared_tiles = true) {
+                        hipEvent_t* ev) {
   MOE_CHECK_LAUNCH(
       moe::launch_permute(ids, static_cast<int>(p.P), p.E, p.T, moe::experts_tile_rows(p.shape),
-                          shared_tiles && p.Is > 0, at<int32_t>(ws, p.rank), at<int32_t>(ws, p.hist),
+                          p.Is > 0, at<int32_t>(ws, p.rank), at<int32_t>(ws, p.hist),
                           at<int32_t>(ws, p.base), offsets, sorted, pos, at<int2>(ws, p.tiles),
                           at<int32_t>(ws, p.ntiles), w, w ? at<float>(ws, p.wsorted) : nullptr,
                           stream, ev),
@@ -230,8 +225,7 @@ moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* rou
   uint16_t* o_shared = p.Is > 0 ? o_routed + static_cast<size_t>(p.P) * p.H : nullptr;
 
   if ((st = route_impl(p, c, x, router_w, router_bias, ids, w, ws, stream, ev))) return st;
-  if ((st = permute_impl(p, ids, offsets, sorted, pos, w, ws, stream, ev ? ev + 2 : nullptr,
-                         !f8)))
+  if ((st = permute_impl(p, ids, offsets, sorted, pos, w, ws, stream, ev ? ev + 2 : nullptr)))
     return st;
 
   moe::ExpertArgs g{};
@@ -267,24 +261,11 @@ moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* rou
     g.s_up = f8->s_up;
     g.s_down = f8->s_down;
   }
-  // FP8: routed tiles run the e4m3 kernels; the shared expert (bf16) runs
-  // from a tile list of its own.
-  moe::ExpertArgs gs = g;
-  if (f8 && p.Is > 0) {
-    gs.tiles = at<int2>(ws, p.stiles);
-    gs.ntiles = at<int32_t>(ws, p.nstiles);
-    MOE_CHECK_LAUNCH(moe::launch_dense_tiles(at<int2>(ws, p.stiles), at<int32_t>(ws, p.nstiles),
-                                             p.T, moe::experts_tile_rows(p.shape), p.E, stream),
-                     "shared tile list");
-  }
+  // FP8: the e4m3 kernels; their blocks on shared-expert tiles run the bf16 body.
   if (ev) hipEventRecord(ev[5], stream);
   MOE_CHECK_LAUNCH(moe::launch_gateup(g, p.shape, p.tile_cap, stream, f8 ? 1 : 0), "gate/up gemm");
-  if (f8 && p.Is > 0)
-    MOE_CHECK_LAUNCH(moe::launch_gateup(gs, p.shape, p.stile_cap, stream, 0), "shared gate/up");
   if (ev) hipEventRecord(ev[6], stream);
   MOE_CHECK_LAUNCH(moe::launch_down(g, p.shape, p.tile_cap, stream, f8 ? 1 : 0), "down gemm");
-  if (f8 && p.Is > 0)
-    MOE_CHECK_LAUNCH(moe::launch_down(gs, p.shape, p.stile_cap, stream, 0), "shared down");
 
   if (ev) hipEventRecord(ev[7], stream);
   MOE_CHECK_LAUNCH(moe::launch_combine(o_routed, o_shared, pos, p.k, p.T, p.H, y, stream),
