@@ -80,10 +80,15 @@ PROFILE_COMMANDS = {
     "pmc_write_copy": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write_copy -o run -- "
                       "python3 bench.py --copy-calibration 1073741824",
 }
-KERNEL_SOURCES = {"expert_gemm": "experts.hip", "router_gemm_kernel": "router.hip",
-                  "topk_kernel": "router.hip", "combine_kernel": "experts.hip",
-                  "permute_small_kernel": "permute.hip", "rank_kernel": "permute.hip",
-                  "scan_kernel": "permute.hip", "scatter_kernel": "permute.hip"}
+# The sources each kernel is built from (its file and the headers it includes).
+_EXPERT_SRC = ("experts.hip", "expert_tile.h", "common.h", "kernels.h")
+_ROUTER_SRC = ("router.hip", "router_ops.h", "common.h", "kernels.h")
+_PERMUTE_SRC = ("permute.hip", "permute_ops.h", "common.h", "kernels.h")
+KERNEL_SOURCES = {"expert_gemm": _EXPERT_SRC, "combine_kernel": _EXPERT_SRC,
+                  "router_gemm_kernel": _ROUTER_SRC, "topk_kernel": _ROUTER_SRC,
+                  "topk_block_kernel": _ROUTER_SRC, "router_split_kernel": _ROUTER_SRC,
+                  "permute_small_kernel": _PERMUTE_SRC, "rank_kernel": _PERMUTE_SRC,
+                  "scan_kernel": _PERMUTE_SRC, "scatter_kernel": _PERMUTE_SRC}
 
 
 def _short(name):
@@ -91,9 +96,13 @@ def _short(name):
     return name.split("(")[0].strip()
 
 
-def _src_sha(fname):
-    path = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", fname)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+def _src_sha(fnames):
+    """SHA-256 over the given kernel sources, in order."""
+    h = hashlib.sha256()
+    for fname in fnames:
+        with open(os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", fname), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def summarize_profiles(d):
@@ -156,7 +165,7 @@ def summarize_profiles(d):
                    "down_kernel" if short.startswith("expert_gemm<1") else base)
             traffic[f"{key}:{wl}"] = {"kernel": short, "read_bytes": rb, "write_bytes": wb,
                                       "bytes_per_launch": rb + wb,
-                                      "source_sha256": _src_sha(KERNEL_SOURCES.get(base, "experts.hip"))}
+                                      "source_sha256": _src_sha(KERNEL_SOURCES.get(base, _EXPERT_SRC))}
     with open(os.path.join(out_dir, "hbm_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(os.path.join(out_dir, "traffic.json"), "w") as f:
@@ -199,7 +208,7 @@ def traffic_for(kernel, workload):
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get(f"{kernel}:{workload}")
-    if not ent or ent.get("source_sha256") != _src_sha("experts.hip"):
+    if not ent or ent.get("source_sha256") != _src_sha(_EXPERT_SRC):
         return None  # counters were taken on another version of the kernel
     return ent.get("bytes_per_launch")
 

@@ -173,6 +173,37 @@ moe_status moe_forward_fp8(const moe_config* cfg, const uint16_t* x, const float
                            const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
                            float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The same layer forward as moe_forward in ONE kernel launch, for small
+ * batches (decoding): tokens <= 256 and tokens * top_k <= 2048, else
+ * MOE_ERR_UNSUPPORTED.
+ *
+ * CURRENTLY SWITCHED OFF: after validating its arguments every call returns
+ * MOE_ERR_UNSUPPORTED and launches nothing.  The kernel did not finish on
+ * its first run on an MI355X and the cause is not yet known; moe_forward
+ * computes the same results.  The contract below is the one the kernel
+ * implements. */
+/* It is the fused expert backend that the sglang-jax issue "[Feature] Support Step 3.5 Flash (StepFun) Model" names as the
+ * performance switch after the grouped-matmul path ("Reuse map",
+ * "Implementation strategy").  Arguments, layouts and outputs are those of
+ * moe_forward, and so are the results, bit for bit: the launch runs the
+ * same tiles in the same arithmetic order.
+ *
+ * Workspace: moe_workspace_size(cfg) bytes, as for moe_forward.  Its
+ * control words (MOE_WS_FUSED_CTL below, under 5 KB) must be zero before
+ * the first moe_forward_fused call on that workspace -- zero-fill the
+ * workspace once after allocating it; every call leaves them zero again,
+ * and no other entry point writes them.  Calls that share a workspace must
+ * be ordered (one stream).  The status word (MOE_WS_FUSED_STATUS) stays
+ * zero unless an internal wait gave up (about a second, only possible if
+ * the launch was starved), which marks the outputs invalid; it is sticky
+ * until the caller clears it. */
+moe_status moe_forward_fused(const moe_config* cfg, const uint16_t* x, const float* router_w,
+                             const float* router_bias, const uint16_t* w_gate,
+                             const uint16_t* w_up, const uint16_t* w_down,
+                             const uint16_t* ws_gate, const uint16_t* ws_up,
+                             const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
+                             float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Where an intermediate of moe_forward lives inside the workspace, for
  * inspection after the stream has finished (tests, debugging).  Writes the
  * byte offset and size; returns MOE_ERR_INVALID_ARG for an unknown id. */
@@ -184,8 +215,10 @@ enum {
   MOE_WS_PAIR_POS = 4,       /* [T*k] int32                                */
   MOE_WS_H = 5,              /* [T*k][I] bf16 routed SwiGLU activations in
                                 sorted order, then [T][Is] shared          */
-  MOE_WS_O = 6               /* [T*k][H] bf16 weighted routed expert outputs
+  MOE_WS_O = 6,              /* [T*k][H] bf16 weighted routed expert outputs
                                 in sorted order, then [T][H] shared        */
+  MOE_WS_FUSED_CTL = 7,      /* uint32 control words of moe_forward_fused  */
+  MOE_WS_FUSED_STATUS = 8    /* uint32: nonzero = a fused wait gave up     */
 };
 moe_status moe_workspace_view(const moe_config* cfg, int which, size_t* offset, size_t* bytes);
 

@@ -22,7 +22,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 STAGES = ("router_gemm", "topk", "rank", "scan", "scatter", "gateup", "down", "combine")
 MOE_NUM_STAGES = len(STAGES)
 (MOE_WS_TOPK_IDS, MOE_WS_TOPK_W, MOE_WS_EXPERT_OFFSETS, MOE_WS_SORTED_PAIRS, MOE_WS_PAIR_POS,
- MOE_WS_H, MOE_WS_O) = range(7)
+ MOE_WS_H, MOE_WS_O, MOE_WS_FUSED_CTL, MOE_WS_FUSED_STATUS) = range(9)
+FUSED_MAX_TOKENS, FUSED_MAX_PAIRS = 256, 2048
 
 
 class MoeError(RuntimeError):
@@ -84,8 +85,9 @@ def load_library():
     lib.moe_dense_workspace_size.argtypes = [dp]
     lib.moe_dense_workspace_size.restype = sz
     lib.moe_dense_forward.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_forward_fused.argtypes = lib.moe_forward.argtypes
     for f in ("moe_route", "moe_permute", "moe_forward", "moe_forward_timed",
-              "moe_workspace_view", "moe_dense_forward", "moe_forward_fp8"):
+              "moe_workspace_view", "moe_dense_forward", "moe_forward_fp8", "moe_forward_fused"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -93,7 +95,7 @@ def load_library():
 
 EXPORTED = ("moe_workspace_size", "moe_last_error", "moe_route", "moe_permute", "moe_forward",
             "moe_forward_timed", "moe_workspace_view", "moe_dense_workspace_size",
-            "moe_dense_forward", "moe_forward_fp8")
+            "moe_dense_forward", "moe_forward_fp8", "moe_forward_fused")
 
 
 # ------------------------------------------------------------------ helpers
@@ -158,9 +160,10 @@ def moe_workspace_size(cfg: moe_config) -> int:
 
 
 def alloc_workspace(cfg: moe_config, device=None):
-    """A uint8 device tensor of moe_workspace_size(cfg) bytes."""
+    """A zero-filled uint8 device tensor of moe_workspace_size(cfg) bytes
+    (zero-filled once, as moe_forward_fused requires of its control words)."""
     torch = _torch()
-    return torch.empty(moe_workspace_size(cfg), dtype=torch.uint8,
+    return torch.zeros(moe_workspace_size(cfg), dtype=torch.uint8,
                        device=device or torch.device("cuda"))
 
 
@@ -200,6 +203,15 @@ def moe_forward(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws
     _check(lib.moe_forward(*_forward_args(cfg, x, router_w, router_bias, w_gate, w_up, w_down,
                                           ws_gate, ws_up, ws_down, y, topk_ids_out, topk_w_out,
                                           ws, stream)))
+
+
+def moe_forward_fused(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                      ws_down, y, topk_ids_out=None, topk_w_out=None, ws=None, stream=None):
+    """moe_forward in a single launch (tokens <= 256, tokens * top_k <= 2048)."""
+    lib = load_library()
+    _check(lib.moe_forward_fused(*_forward_args(cfg, x, router_w, router_bias, w_gate, w_up,
+                                                w_down, ws_gate, ws_up, ws_down, y, topk_ids_out,
+                                                topk_w_out, ws, stream)))
 
 
 def moe_forward_timed(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up,

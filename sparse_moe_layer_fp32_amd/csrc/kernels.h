@@ -49,8 +49,58 @@ struct ExpertArgs {
   int Np;                   // rows of wsplit (a multiple of the column tile)
 };
 
+// Single-launch forward for small batches (fused.hip).  Control words live
+// in the workspace: words [0, kCtlReset) are zero before a launch and the
+// last block to finish sets them back to zero; kCtlStatus collects the
+// flags of waits that ran out (sticky).
+constexpr int kFusedMaxTokens = 256;
+constexpr int kFusedMaxPairs = 2048;
+constexpr int kFusedMaxRoutedTiles = kFusedMaxPairs / 64 + kMaxExperts;
+constexpr int kFusedMaxSharedTiles = kFusedMaxTokens / 64;
+enum FusedCtl : int {
+  kCtlTicket = 0,        // one ticket counter per phase (8)
+  kCtlRouterDone = 8,    // router tiles finished
+  kCtlTopkDone = 9,      // top-k units finished
+  kCtlPermDone = 10,     // permutation published (0 / 1)
+  kCtlDownDone = 11,     // down tiles finished (shared and routed)
+  kCtlExit = 12,         // blocks finished
+  kCtlNtiles = 13,       // routed row tiles (valid once kCtlPermDone is set)
+  kCtlSharedGu = 16,     // per shared row tile: gate/up tiles finished
+  kCtlTileGu = kCtlSharedGu + kFusedMaxSharedTiles,  // per routed row tile: the same
+  kCtlReset = kCtlTileGu + kFusedMaxRoutedTiles,
+  kCtlStatus = kCtlReset,
+  kCtlWords = (kCtlReset + 1 + 63) / 64 * 64,
+};
+// kCtlStatus bits: which wait gave up.
+enum FusedStatus : uint32_t {
+  kStRouter = 1, kStTopk = 2, kStPerm = 4, kStSharedGu = 8, kStGu = 16, kStDown = 32,
+};
+
 constexpr int kTileBig = 0;    // 256 x 256 tiles
 constexpr int kTileSmall = 1;  // 64 x 128 tiles
+
+// Arguments of the single-launch forward: the expert GEMMs' arguments plus
+// the router's, the buffers the permutation writes and the control words.
+struct FusedArgs {
+  ExpertArgs g;
+  const float* wg;      // [E][H]
+  const float* bias;    // [E] or null
+  float* zpart;         // [T][E][S] router partial logits
+  int S;                // router k splits
+  float scaling;
+  int renorm;
+  int32_t* ids;         // [T][k]
+  float* w;             // [T][k]
+  int32_t* offsets;     // [E+1]     (g.offsets, writable)
+  int32_t* sorted;      // [P]       (g.sorted)
+  float* w_sorted;      // [P]       (g.w_sorted)
+  int32_t* pos;         // [P]
+  int2* tiles;          // routed row tiles of 64 rows
+  int tile_cap;         // capacity of tiles
+  uint16_t* y;          // [T][H]
+  uint32_t* ctl;        // kCtlWords control words
+};
+hipError_t launch_fused(const FusedArgs& f, hipStream_t stream);
 
 // router.hip
 int router_split(int T, int H, int E);

@@ -1,6 +1,8 @@
 import os
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -8,3 +10,17 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def full_experts():
+    """Expert weights of the full-shape workloads (identical recipe and seed
+    for decode, prefill, skewed and long; 9.1 GB), generated once per
+    session, host + device."""
+    import synth
+    from tests import gpu_util as gu
+    wl = synth.WORKLOADS["decode"]
+    gu.note("  generating full-shape expert weights (9.1 GB)")
+    host = synth.gen_experts(wl)
+    dev = tuple(gu.to_dev(a) for a in host)
+    return host, dev

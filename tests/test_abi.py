@@ -148,3 +148,31 @@ def test_dense_errors_before_launch():
     bad.reserved = 1
     st = lib.moe_dense_forward(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, need, None)
     assert st == moe.MOE_ERR_INVALID_ARG
+
+
+def test_fused_errors_before_launch():
+    """moe_forward_fused: the batch limits, NULLs and the workspace size are
+    checked before anything is enqueued; the workspace views of its control
+    and status words lie inside the workspace."""
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    cfg = full(64)
+    need = moe.moe_workspace_size(cfg)
+    args = [fake, fake, None, fake, fake, fake, fake, fake, fake, fake, None, None, fake]
+    st = lib.moe_forward_fused(ctypes.byref(cfg), *args, need - 1, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    null_x = [None] + args[1:]
+    st = lib.moe_forward_fused(ctypes.byref(cfg), *null_x, need, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    for T, k in ((moe.FUSED_MAX_TOKENS + 1, 8), (moe.FUSED_MAX_TOKENS, 9)):
+        big = moe.make_config(T, 4096, 288, k, 1280, 1280)
+        st = lib.moe_forward_fused(ctypes.byref(big), *args, moe.moe_workspace_size(big), None)
+        assert st == moe.MOE_ERR_UNSUPPORTED and "single-launch" in moe.moe_last_error()
+    # switched off: a valid call is refused before anything is launched
+    st = lib.moe_forward_fused(ctypes.byref(cfg), *args, need, None)
+    assert st == moe.MOE_ERR_UNSUPPORTED and "switched off" in moe.moe_last_error()
+    total = moe.moe_workspace_size(cfg)
+    c_off, c_nb = moe.moe_workspace_view(cfg, moe.MOE_WS_FUSED_CTL)
+    s_off, s_nb = moe.moe_workspace_view(cfg, moe.MOE_WS_FUSED_STATUS)
+    assert c_off + c_nb <= total and c_nb % 256 == 0 and s_nb == 4
+    assert c_off <= s_off < c_off + c_nb

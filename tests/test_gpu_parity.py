@@ -248,17 +248,6 @@ def test_errors_enqueue_nothing(moe):
 
 # ------------------------------------------------------------- full shapes
 
-@pytest.fixture(scope="module")
-def full_experts():
-    """Expert weights of the full-shape workloads (identical recipe and seed
-    for decode, prefill, skewed and long), generated once, host + device."""
-    wl = synth.WORKLOADS["decode"]
-    gu.note("  generating full-shape expert weights (9.1 GB)")
-    host = synth.gen_experts(wl)
-    dev = tuple(gu.to_dev(a) for a in host)
-    return host, dev
-
-
 def _sample_tokens(T, extra=()):
     rng = np.random.default_rng(T)
     base = list(range(min(T, 8))) + list(range(max(0, T - 8), T))
