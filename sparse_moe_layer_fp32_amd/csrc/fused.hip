@@ -303,8 +303,8 @@ __global__ __launch_bounds__(kFT) void fused_kernel(FusedArgs f) {
         float* zl = reinterpret_cast<float*>(smem) + wv * kMaxExperts;
         uint64_t* kl = reinterpret_cast<uint64_t*>(smem + 4 * kMaxExperts * 4) + wv * kMaxExperts;
         if (tok < s.T)
-          topk_wave_lds(f.zpart, s.S, static_cast<int64_t>(E) * s.S, f.bias, E, f.g.k, f.scaling,
-                        f.renorm, f.ids, f.w, tok, zl, kl);
+          topk_wave_lds(f.zpart, f.pl, f.bias, E, f.g.k, f.scaling, f.renorm, f.ids, f.w, tok,
+                        zl, kl);
         block_signal(ctl, kCtlTopkDone);
         break;
       }

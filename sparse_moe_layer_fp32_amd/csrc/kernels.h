@@ -12,6 +12,13 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kTopkBlockTokens = 2048;  // below: one top-k block per token
 
+// Where the router's partial logits live: partial s of logit (t, e) is
+// zpart[t ld + e es + s ps], summed over s = 0 .. S-1 in order.
+struct PartialLayout {
+  int S;
+  int64_t ld, es, ps;
+};
+
 // Arguments of the grouped expert GEMMs (gate/up and down share them).
 struct ExpertArgs {
   const uint16_t* x;        // [T][H]
@@ -87,6 +94,7 @@ struct FusedArgs {
   const float* bias;    // [E] or null
   float* zpart;         // [T][E][S] router partial logits
   int S;                // router k splits
+  PartialLayout pl;     // where the partials live
   float scaling;
   int renorm;
   int32_t* ids;         // [T][k]
@@ -113,7 +121,7 @@ hipError_t launch_router_split(const float* wg, int E, int H, int Np, uint16_t* 
 hipError_t launch_router_logits(const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* zpart, int T, int H,
                               int E, int S, hipStream_t stream);
-hipError_t launch_topk(const float* zpart, int S, int64_t ld, const float* bias, int T, int E,
+hipError_t launch_topk(const float* zpart, PartialLayout pl, const float* bias, int T, int E,
                        int k, float scaling, int renorm, int32_t* ids, float* w,
                        hipStream_t stream);
 

@@ -38,7 +38,7 @@ struct Plan {
   int S;         // partials per logit: k splits, or 3 weight planes (router GEMM form)
   int rgemm;     // router logits as one GEMM over the weight planes
   int Np;        // router GEMM: rows of the plane matrix (3E rounded up to the column tile)
-  int64_t zld;   // row stride of the partial logits
+  int64_t zld;   // partial logits per token (E S, or Np for the plane GEMM)
   int C;         // permutation chunks, padded to a multiple of 4
   int shape;     // expert GEMM tile shape (kTileBig / kTileSmall)
   int tile_cap;  // capacity of the GEMM tile list
@@ -142,6 +142,13 @@ moe_status check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+// Split-k partials are planes [S][T][E]; the plane GEMM's are rows [T][Np]
+// with the three planes of expert e in columns 3e .. 3e+2.
+moe::PartialLayout partial_layout(const Plan& p) {
+  if (p.rgemm) return {3, p.Np, 3, 1};
+  return {p.S, p.E, 1, p.T * p.E};
+}
+
 moe_status route_impl(const Plan& p, const moe_config* c, const uint16_t* x, const float* rw,
                       const float* rb, int32_t* ids, float* w, void* ws, hipStream_t stream,
                       hipEvent_t* ev) {
@@ -164,7 +171,7 @@ moe_status route_impl(const Plan& p, const moe_config* c, const uint16_t* x, con
                      "router gemm");
   }
   if (ev) hipEventRecord(ev[1], stream);
-  MOE_CHECK_LAUNCH(moe::launch_topk(zpart, p.S, p.zld, rb, T, p.E, p.k, c->routed_scaling,
+  MOE_CHECK_LAUNCH(moe::launch_topk(zpart, partial_layout(p), rb, T, p.E, p.k, c->routed_scaling,
                                     c->renormalize ? 1 : 0, ids, w, stream),
                    "top-k");
   return MOE_OK;
@@ -327,6 +334,7 @@ moe_status forward_fused_impl(const moe_config* c, const uint16_t* x, const floa
   f.bias = router_bias;
   f.zpart = at<float>(ws, p.zpart);
   f.S = p.S;
+  f.pl = partial_layout(p);
   f.scaling = c->routed_scaling;
   f.renorm = c->renormalize ? 1 : 0;
   f.ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.ids);

@@ -19,15 +19,15 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 
 // One wave per token (topk_wave).
 template <int NS>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpart, int S,
-                                                   int64_t ld, const float* __restrict__ bias,
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpart,
+                                                   PartialLayout pl, const float* __restrict__ bias,
                                                    int T, int E,
                                                    int k, float scaling, int renorm,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
   const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;
-  topk_wave<NS>(zpart, S, ld, bias, E, k, scaling, renorm, ids, w, t);
+  topk_wave<NS>(zpart, pl, bias, E, k, scaling, renorm, ids, w, t);
 }
 
 // Few tokens, many partials: one block per token with one thread per expert
@@ -39,8 +39,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zpa
 constexpr int TKB_MAX_WAVES = kMaxExperts / 64;
 constexpr int TKB_PER_LANE = TKB_MAX_WAVES * kMaxTopK / 64;  // merge candidates per lane
 
-__global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restrict__ zpart, int S,
-                                                          int64_t ld,
+__global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restrict__ zpart,
+                                                          PartialLayout pl,
                                                           const float* __restrict__ bias, int T,
                                                           int E, int k, float scaling,
                                                           int renorm, int32_t* __restrict__ ids,
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
   float z = 0.f;
   uint64_t key = 0;
   if (e < E) {
-    z = sum_splits(zpart + static_cast<int64_t>(t) * ld + static_cast<int64_t>(e) * S, S);
+    z = sum_partials(zpart + t * pl.ld + e * pl.es, pl.S, pl.ps);
     float kv = sigmoid_f32(z) + (bias ? bias[e] : 0.f);
     if (kv != kv) kv = -INFINITY;
     key = (static_cast<uint64_t>(orderable(kv)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
@@ -168,13 +168,13 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* zpart, 
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* zpart, int S, int64_t ld, const float* bias, int T, int E,
+hipError_t launch_topk(const float* zpart, PartialLayout pl, const float* bias, int T, int E,
                        int k, float scaling, int renorm, int32_t* ids, float* w,
                        hipStream_t stream) {
   if (T < kTopkBlockTokens) {
     // Few tokens: a block per token spreads the partial sums over more CUs.
     const int threads = (E + 63) / 64 * 64;
-    topk_block_kernel<<<T, threads, 0, stream>>>(zpart, S, ld, bias, T, E, k, scaling, renorm,
+    topk_block_kernel<<<T, threads, 0, stream>>>(zpart, pl, bias, T, E, k, scaling, renorm,
                                                  ids, w);
     return hipGetLastError();
   }
@@ -183,7 +183,7 @@ hipError_t launch_topk(const float* zpart, int S, int64_t ld, const float* bias,
   switch (ns) {
 #define MOE_TOPK_CASE(N) \
   case N:                \
-    topk_kernel<N><<<blocks, 256, 0, stream>>>(zpart, S, ld, bias, T, E, k, scaling, renorm, ids, \
+    topk_kernel<N><<<blocks, 256, 0, stream>>>(zpart, pl, bias, T, E, k, scaling, renorm, ids, \
                                                w); \
     break;
     MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4) MOE_TOPK_CASE(5)

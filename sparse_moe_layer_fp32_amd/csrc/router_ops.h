@@ -38,8 +38,8 @@ __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uin
   lo = f32_to_bf16_bits(r2);
 }
 
-// zpart[t][e][s] = sum over k in split s of x[t][k] * wg[e][k] (the split
-// partials of one logit are contiguous, S a power of two <= 32).
+// zpart[s][t][e] = sum over k in split s of x[t][k] * wg[e][k] (one
+// contiguous [T][E] plane per split, S a power of two <= 32).
 // One 64 x 64 tile (experts bx, tokens by) of split s; 256 threads = 4 waves
 // in a 2x2 layout, each wave one 32x32 output block; smem holds
 // kRouterTileLds bytes (two stages of x and of the three weight planes).
@@ -148,7 +148,7 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = m0 + 32 * wm + mfma32_row(r, lane);
-      if (t < T) zpart[(static_cast<int64_t>(t) * E + e) * nsplit + s] = acc[r];
+      if (t < T) zpart[(static_cast<int64_t>(s) * T + t) * E + e] = acc[r];
     }
   }
 }
@@ -197,32 +197,26 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return a > b ? a : b;
 }
 
-// Sum of the S partials of one logit, in order (S a power of two <= 32 for
-// k splits, or 3 for the weight planes; the partials of one logit are
-// contiguous).
-__device__ __forceinline__ float sum_splits(const float* p, int S) {
-  if (S == 1) return p[0];
-  if (S == 2) {
-    const float2 a = *reinterpret_cast<const float2*>(p);
-    return a.x + a.y;
-  }
-  if (S == 3) return (p[0] + p[1]) + p[2];  // the three weight planes, hi + mid + lo
-  f32x4 v[8];
+// Sum of the S <= 32 partials of one logit in order, p0 + p1 + ... (k
+// splits, or the three weight planes hi + mid + lo); partial i is at p[i ps].
+__device__ __forceinline__ float sum_partials(const float* p, int S, int64_t ps) {
+  float v[32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (4 * i < S) v[i] = *reinterpret_cast<const f32x4*>(p + 4 * i);
-  float acc = v[0][0];
+  for (int i = 0; i < 32; ++i)
+    if (i < S) {
+      v[i] = *p;
+      p += ps;
+    }
+  float acc = v[0];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (4 * i < S)
-#pragma unroll
-      for (int q = (i == 0 ? 1 : 0); q < 4; ++q) acc += v[i][q];
+  for (int i = 1; i < 32; ++i)
+    if (i < S) acc += v[i];
   return acc;
 }
 
 // Top-k of token t by the calling wave (see above).
 template <int NS>
-__device__ __forceinline__ void topk_wave(const float* __restrict__ zpart, int S, int64_t ld,
+__device__ __forceinline__ void topk_wave(const float* __restrict__ zpart, PartialLayout pl,
                                           const float* __restrict__ bias, int E, int k,
                                           float scaling, int renorm, int32_t* __restrict__ ids,
                                           float* __restrict__ w, int t) {
@@ -235,7 +229,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ zpart, int S
     z[i] = 0.f;
     key[i] = 0;  // below every real key: never selected
     if (e < E) {
-      z[i] = sum_splits(zpart + static_cast<int64_t>(t) * ld + static_cast<int64_t>(e) * S, S);
+      z[i] = sum_partials(zpart + t * pl.ld + e * pl.es, pl.S, pl.ps);
       float kv = sigmoid_f32(z[i]) + (bias ? bias[e] : 0.f);
       if (kv != kv) kv = -INFINITY;  // non-finite input: rank last, stay in range
       key[i] = (static_cast<uint64_t>(orderable(kv)) << 32) |
@@ -281,7 +275,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ zpart, int S
 // logits and keys.  The partials are read two slots at a time (bounded
 // registers).  Keys, scores, the selection and the sums are those of
 // topk_wave, so the results are identical.
-__device__ __forceinline__ void topk_wave_lds(const float* __restrict__ zpart, int S, int64_t ld,
+__device__ __forceinline__ void topk_wave_lds(const float* __restrict__ zpart, PartialLayout pl,
                                               const float* __restrict__ bias, int E, int k,
                                               float scaling, int renorm,
                                               int32_t* __restrict__ ids, float* __restrict__ w,
@@ -295,7 +289,7 @@ __device__ __forceinline__ void topk_wave_lds(const float* __restrict__ zpart, i
       const int e = lane + 64 * (i0 + j);
       z[j] = 0.f;
       if (e < E)
-        z[j] = sum_splits(zpart + static_cast<int64_t>(t) * ld + static_cast<int64_t>(e) * S, S);
+        z[j] = sum_partials(zpart + t * pl.ld + e * pl.es, pl.S, pl.ps);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
