@@ -19,8 +19,8 @@
 //    k-contiguous in memory (weights are out x in), so A and B fragments are
 //    plain 16-byte LDS reads.
 //  * Tiles are copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR
-//    staging): one wave instruction fills 1 KiB of LDS (8 rows of a 64-wide
-//    k step, or 16 rows of a 32-wide one); rows are gathered per lane, so
+//    staging): one wave instruction fills 1 KiB of LDS (4, 8 or 16 rows of
+//    a 128-, 64- or 32-wide k step); rows are gathered per lane, so
 //    the token gather of the gate/up GEMM costs nothing extra.  The 16-byte
 //    chunks of a row are XOR-swizzled so that the 64 lanes of a fragment
 //    read hit all 64 LDS banks once (no bank conflicts).
@@ -31,9 +31,9 @@
 //    are spread over the 8 XCDs in contiguous ranges and walked in groups of
 //    8 row tiles so that co-resident blocks share operands in their L2.
 //
-// Two tile shapes: 256 x 256 (one block per CU, 8 waves of 128 x 64) for
-// many rows per expert, and 64 x 128 with a 3-deep ring (two blocks per CU)
-// for few rows per expert, where the GEMMs stream weights at HBM rate.
+// Two tile families: 256 x 256 (one block per CU, 8 waves of 128 x 64) for
+// many rows per expert, and 64-row tiles with a 3-deep ring for few rows per
+// expert, where the GEMMs stream weights at HBM rate.
 
 #pragma once
 
@@ -93,25 +93,29 @@ struct Cfg {
   static constexpr int KS = BK / 16;          // MFMA k-substeps per stage
   static constexpr int STAGE_BYTES = BM * ROWB + BN * BROWB;
   static constexpr int LDS_BYTES = S * STAGE_BYTES;
-  static_assert(CH == 4 || CH == 8, "k step of 32 or 64");
-  static_assert(CHB == 2 || CHB == 4 || CHB == 8, "B row of 32, 64 or 128 bytes");
+  static_assert(CH == 4 || CH == 8 || CH == 16, "k step of 32, 64 or 128");
+  static_assert(CHB == 2 || CHB == 4 || CHB == 8 || CHB == 16, "B row of 32 to 256 bytes");
   static_assert(MB >= 1 && NB >= 1 && JA >= 1 && JB >= 1, "tile shape");
   static_assert(NI * (S > 2 ? S - 2 : 1) <= 63, "vmcnt budget");
   // XOR swizzle of a row's 16-byte chunks.  The LDS serves 16 lanes (256
   // bytes, 64 banks) per cycle; a fragment read has those 16 lanes on 16
-  // consecutive rows at one logical chunk.  With 128-byte rows, even and odd
-  // rows fall in different bank halves and (row >> 1) & 7 spreads the 8 rows
-  // of each half over its 8 chunk slots; with 64-byte rows, row & 3 picks the
-  // quarter and (row >> 2) & 3 the slot.  Either way the 16 lanes hit 16
-  // distinct 16-byte bank groups.
+  // consecutive rows at one logical chunk.  With 256-byte rows every row
+  // spans all banks and row & 15 gives the 16 rows 16 different chunk slots;
+  // with 128-byte rows, even and odd rows fall in different bank halves and
+  // (row >> 1) & 7 spreads the 8 rows of each half over its 8 chunk slots;
+  // with 64-byte rows, row & 3 picks the quarter and (row >> 2) & 3 the
+  // slot.  Either way the 16 lanes hit 16 distinct 16-byte bank groups.
   static __device__ __forceinline__ int swz(int row) {
-    return CH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+    return CH == 16 ? (row & 15) : CH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
   }
   // B rows: as above for bf16.  e4m3 fragments are 8-byte reads of 64- or
   // 32-byte rows (32 lanes per cycle); the swizzle spreads the rows that
   // share a bank window over the chunk slots (at most two lanes per bank).
   static __device__ __forceinline__ int swzb(int row) {
-    return CHB == 8 ? ((row >> 1) & 7) : CHB == 4 ? ((row >> 2) & 3) : ((row >> 3) & 1);
+    return CHB == 16  ? (row & 15)
+           : CHB == 8 ? ((row >> 1) & 7)
+           : CHB == 4 ? ((row >> 2) & 3)
+                      : ((row >> 3) & 1);
   }
 };
 

@@ -82,8 +82,12 @@ int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape) {
 
 // Tile shapes: big = 256 x 256, k step 32, 4-deep ring with two stages in
 // flight, 8 waves of 128 x 64 (two per SIMD, so one wave's stalls are
-// covered by the other's MFMAs); small = 64 x 128, k step 64, 3-deep ring,
-// 4 waves, two blocks per CU.
+// covered by the other's MFMAs).  Small (few rows per expert, the GEMMs
+// stream weights): 64 rows, 3-deep ring, one block per CU; gate/up 64 h
+// columns (128 weight rows) with k step 128, so every weight row is read in
+// 256-byte pieces; down 256 output columns, k step 64, 8 waves (128 columns
+// and 4 waves when H is not a multiple of 256).  The e4m3 kernels keep
+// 64 x 128 tiles with k step 64.
 hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream,
                          int fp8) {
   const int maxn = std::max(a.I, a.Is);
@@ -94,7 +98,7 @@ hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipS
   }
   if (shape == kTileBig)
     return launch_one<0, 256, 256, 32, 2, 4, 4>(a, tile_capacity, (maxn + 127) / 128, stream);
-  return launch_one<0, 64, 128, 64, 2, 2, 3>(a, tile_capacity, (maxn + 63) / 64, stream);
+  return launch_one<0, 64, 128, 128, 2, 2, 3>(a, tile_capacity, (maxn + 63) / 64, stream);
 }
 
 hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream,
@@ -106,6 +110,8 @@ hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStr
   }
   if (shape == kTileBig)
     return launch_one<1, 256, 256, 32, 2, 4, 4>(a, tile_capacity, a.H / 256, stream);
+  if (a.H % 256 == 0)
+    return launch_one<1, 64, 256, 64, 2, 4, 3>(a, tile_capacity, a.H / 256, stream);
   return launch_one<1, 64, 128, 64, 2, 2, 3>(a, tile_capacity, a.H / 128, stream);
 }
 

@@ -84,7 +84,7 @@ enum FusedStatus : uint32_t {
 };
 
 constexpr int kTileBig = 0;    // 256 x 256 tiles
-constexpr int kTileSmall = 1;  // 64 x 128 tiles
+constexpr int kTileSmall = 1;  // 64-row tiles
 
 // Arguments of the single-launch forward: the expert GEMMs' arguments plus
 // the router's, the buffers the permutation writes and the control words.
