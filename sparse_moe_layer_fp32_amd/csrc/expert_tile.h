@@ -75,7 +75,9 @@ __device__ __forceinline__ TileCoord tile_of(int u, int ntiles, int NT) {
   return {first + within % gm, within / gm};
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int S, int WF = 0>
+// AV = 1 (split ring): A goes through its own 2-deep LDS ring, one k step
+// ahead; B through an S-deep ring, S-1 steps ahead.
+template <int BM, int BN, int BK, int WM, int WN, int S, int WF = 0, int AV = 0>
 struct Cfg {
   static constexpr int NW = WM * WN;
   static constexpr int THREADS = 64 * NW;
@@ -92,7 +94,9 @@ struct Cfg {
   static constexpr int NI = JA + JB;
   static constexpr int KS = BK / 16;          // MFMA k-substeps per stage
   static constexpr int STAGE_BYTES = BM * ROWB + BN * BROWB;
-  static constexpr int LDS_BYTES = S * STAGE_BYTES;
+  static constexpr int A_BYTES = BM * ROWB;   // one A buffer (AV)
+  static constexpr int B_BYTES = BN * BROWB;  // one B buffer (AV)
+  static constexpr int LDS_BYTES = AV ? 2 * A_BYTES + S * B_BYTES : S * STAGE_BYTES;
   static_assert(CH == 4 || CH == 8 || CH == 16, "k step of 32, 64 or 128");
   static_assert(CHB == 2 || CHB == 4 || CHB == 8 || CHB == 16, "B row of 32 to 256 bytes");
   static_assert(MB >= 1 && NB >= 1 && JA >= 1 && JB >= 1, "tile shape");
@@ -127,10 +131,11 @@ struct Cfg {
 // row's scale in the epilogue (a scale per output row factors out of the
 // dot product).  The shared expert's tiles (bf16 weights) in such a launch
 // take the bf16 body: the choice is made once per block.
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF, int AV = 0>
 __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, TileCoord tc,
                                           int e, int row0) {
-  using C = Cfg<BM, BN, BK, WM, WN, S, WF>;
+  using C = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
+  static_assert(AV == 0 || (WF == 0 && S >= 3), "split ring: bf16, B ring of >= 3");
   using BT = typename std::conditional<WF == 1, uint8_t, uint16_t>::type;
   static_assert(WF == 0 || MODE < 2, "e4m3 weights are for the expert GEMMs");
   const bool shared = MODE != 2 && e == a.E;
@@ -252,7 +257,7 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
     } else {
       brow = wn * (BN / WN) + 32 * nb;
     }
-    b_off[nb] = BM * C::ROWB + (brow + fr) * C::BROWB;
+    b_off[nb] = (AV ? 0 : BM * C::ROWB) + (brow + fr) * C::BROWB;
   }
 
   const int KT = K / BK;
@@ -275,7 +280,10 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
   bf16x8 af[2][C::MB], bf[2][C::NB];
   const int fswzb = C::swzb(fr);
   auto load_frags = [&](int kt, int ks, int set) {
-    const uint8_t* st = smem + (kt % S) * C::STAGE_BYTES;
+    // A and B of stage kt: one ring slot, or (AV) the A and B buffers
+    const uint8_t* st =
+        AV ? smem + 2 * C::A_BYTES + (kt % S) * C::B_BYTES : smem + (kt % S) * C::STAGE_BYTES;
+    const uint8_t* sa = AV ? smem + (kt & 1) * C::A_BYTES : st;
     const int sw = ((2 * ks + fh) ^ fswz) * 16;
     if constexpr (WF == 1) {
       // Logical chunk ks of the e4m3 row holds the 16 codes of k-substep ks;
@@ -294,7 +302,7 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
     }
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
-      af[set][mb] = *reinterpret_cast<const bf16x8*>(st + a_off[mb] + sw);
+      af[set][mb] = *reinterpret_cast<const bf16x8*>(sa + a_off[mb] + sw);
   };
   // The MFMAs of one k-substep; `dma(i)` may issue a refill DMA after MFMA i.
   auto mfmas = [&](int set, auto dma) {
@@ -310,7 +318,79 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
   // (a full fence would); the "memory" clobber keeps LDS accesses in place.
   auto barrier = [] { asm volatile("s_barrier" ::: "memory"); };
 
-  if constexpr (S >= 4) {
+  if constexpr (AV) {
+    // Split ring: A has its own 2-deep ring (one stage ahead), B an S-deep
+    // ring (S-1 stages ahead), both filled by DMA.  Step kt multiplies A(kt)
+    // (A buffer kt & 1) by B(kt) (B slot kt % S).  Right after the barrier
+    // that starts it, A(kt+1) is DMA'd into A buffer (kt+1) & 1; between its
+    // MFMAs, B(kt+S-1) into B slot (kt-1) % S; both were last read in step
+    // kt-1.  At its end, loads returning in order, only B(kt+S-1) may still
+    // be in flight (B(kt+1) was issued in an earlier step), and one barrier
+    // publishes A(kt+1) and B(kt+1).
+    static_assert(S >= 3, "B ring of 3 or more");
+    auto a_issue = [&](int kt) {
+#pragma unroll
+      for (int j = 0; j < C::JA; ++j)
+        dma16(abase + aoff[j] + kt * BK, smem + (kt & 1) * C::A_BYTES + (wid * C::JA + j) * 1024);
+    };
+    auto b_issue = [&](int kt, int j) {
+      dma16(bmat + boff[j] + kt * BK,
+            smem + 2 * C::A_BYTES + (kt % S) * C::B_BYTES + (wid * C::JB + j) * 1024);
+    };
+    auto step_end = [&](int kt) {
+      if (kt + S - 1 < KT)
+        wait_vmcnt<C::JB>();
+      else
+        wait_vmcnt<0>();
+      barrier();
+    };
+    // Prologue: A(0), B(0 .. S-2); wait for A(0) and B(0).
+    a_issue(0);
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < KT)
+#pragma unroll
+        for (int j = 0; j < C::JB; ++j) b_issue(s, j);
+    if (S - 2 < KT)
+      wait_vmcnt<(S - 2) * C::JB>();  // B(1 .. S-2) may be in flight
+    else
+      wait_vmcnt<0>();
+    barrier();
+    constexpr int MFMAS = C::KS * C::MB * C::NB;
+    constexpr int DMA_EVERY = MFMAS / C::JB > 0 ? MFMAS / C::JB : 1;
+    if (!has_rows) {
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) a_issue(kt + 1);
+        if (kt + S - 1 < KT)
+#pragma unroll
+          for (int j = 0; j < C::JB; ++j) b_issue(kt + S - 1, j);
+        if (kt + 1 < KT) step_end(kt);
+      }
+      return;
+    }
+    auto step = [&](int kt, auto REFILL) {
+      constexpr bool refill = decltype(REFILL)::value;
+      if (kt + 1 < KT) a_issue(kt + 1);
+      load_frags(kt, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + 1 < C::KS) load_frags(kt, ks + 1, (ks + 1) & 1);
+        mfmas(ks & 1, [&](int i) {
+          const int g = ks * C::MB * C::NB + i;
+          if (refill && g % DMA_EVERY == DMA_EVERY - 1 && g / DMA_EVERY < C::JB)
+            b_issue(kt + S - 1, g / DMA_EVERY);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (refill && MFMAS / DMA_EVERY < C::JB)
+#pragma unroll
+        for (int j = MFMAS / DMA_EVERY; j < C::JB; ++j) b_issue(kt + S - 1, j);
+      if (kt + 1 < KT) step_end(kt);
+    };
+    int kt = 0;
+    for (; kt + S - 1 < KT; ++kt) step(kt, std::true_type{});
+    for (; kt < KT; ++kt) step(kt, std::false_type{});
+  } else if constexpr (S >= 4) {
     // Ring of S >= 4 buffers, two stages in flight.  Step kt: refill stage
     // kt+2 (buffer of stage kt-2) during the first half of stage kt's MFMAs;
     // mid-stage, wait for stage kt+1 and pass the barrier that publishes it;

@@ -8,10 +8,10 @@ namespace moe {
 
 namespace {
 
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0, int AV = 0>
 __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
-  using C0 = Cfg<BM, BN, BK, WM, WN, S, 0>;
-  using C1 = Cfg<BM, BN, BK, WM, WN, S, WF>;
+  using C0 = Cfg<BM, BN, BK, WM, WN, S, 0, AV>;
+  using C1 = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
   constexpr int LDS = C0::LDS_BYTES > C1::LDS_BYTES ? C0::LDS_BYTES : C1::LDS_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
 
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
       return;
     }
   }
-  gemm_tile<MODE, BM, BN, BK, WM, WN, S, WF>(a, smem, tc, e, row0);
+  gemm_tile<MODE, BM, BN, BK, WM, WN, S, WF, AV>(a, smem, tc, e, row0);
 }
 
 // One thread per 8 consecutive outputs (combine_row).
@@ -47,15 +47,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
               static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
 }
 
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0, int AV = 0>
 hipError_t launch_one(const ExpertArgs& a, int tile_capacity, int NT, hipStream_t stream) {
-  using C = Cfg<BM, BN, BK, WM, WN, S, WF>;
+  using C = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
   const int64_t units = static_cast<int64_t>(tile_capacity) * NT;
   const int64_t grid = (units + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid <= 0) return hipSuccess;
   ExpertArgs b = a;
   b.NT = NT;
-  expert_gemm<MODE, BM, BN, BK, WM, WN, S, WF>
+  expert_gemm<MODE, BM, BN, BK, WM, WN, S, WF, AV>
       <<<static_cast<unsigned>(grid), C::THREADS, 0, stream>>>(b);
   return hipGetLastError();
 }
@@ -80,14 +80,15 @@ int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape) {
   return static_cast<int>(routed + sh);
 }
 
-// Tile shapes: big = 256 x 256, k step 32, 4-deep ring with two stages in
-// flight, 8 waves of 128 x 64 (two per SIMD, so one wave's stalls are
-// covered by the other's MFMAs).  Small (few rows per expert, the GEMMs
-// stream weights): 64 rows, 3-deep ring, one block per CU; gate/up 64 h
-// columns (128 weight rows) with k step 128, so every weight row is read in
-// 256-byte pieces; down 256 output columns, k step 64, 8 waves (128 columns
-// and 4 waves when H is not a multiple of 256).  The e4m3 kernels keep
-// 64 x 128 tiles with k step 64.
+// Tile shapes.  Big (many rows per expert): 256 x 256, k step 64 (128-byte
+// row pieces), 8 waves of 128 x 64 (two per SIMD, so one wave's stalls are
+// covered by the other's MFMAs), split ring with A 2-deep and B 3-deep, the
+// whole 160 KB of LDS; the e4m3 launches keep k step 32 and a 4-deep ring.
+// Small (few rows per expert, the GEMMs stream weights): 64 rows, 3-deep
+// ring, one block per CU; gate/up 64 h columns (128 weight rows) with k step
+// 128, so every weight row is read in 256-byte pieces; down 256 output
+// columns, k step 64, 8 waves (128 columns and 4 waves when H is not a
+// multiple of 256).  The e4m3 kernels keep 64 x 128 tiles with k step 64.
 hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream,
                          int fp8) {
   const int maxn = std::max(a.I, a.Is);
@@ -97,7 +98,8 @@ hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipS
     return launch_one<0, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, (maxn + 63) / 64, stream);
   }
   if (shape == kTileBig)
-    return launch_one<0, 256, 256, 32, 2, 4, 4>(a, tile_capacity, (maxn + 127) / 128, stream);
+    return launch_one<0, 256, 256, 64, 2, 4, 3, 0, 1>(a, tile_capacity, (maxn + 127) / 128,
+                                                      stream);
   return launch_one<0, 64, 128, 128, 2, 2, 3>(a, tile_capacity, (maxn + 63) / 64, stream);
 }
 
@@ -109,7 +111,7 @@ hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStr
     return launch_one<1, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, a.H / 128, stream);
   }
   if (shape == kTileBig)
-    return launch_one<1, 256, 256, 32, 2, 4, 4>(a, tile_capacity, a.H / 256, stream);
+    return launch_one<1, 256, 256, 64, 2, 4, 3, 0, 1>(a, tile_capacity, a.H / 256, stream);
   if (a.H % 256 == 0)
     return launch_one<1, 64, 256, 64, 2, 4, 3>(a, tile_capacity, a.H / 256, stream);
   return launch_one<1, 64, 128, 64, 2, 2, 3>(a, tile_capacity, a.H / 128, stream);
