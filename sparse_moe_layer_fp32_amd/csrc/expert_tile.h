@@ -135,7 +135,7 @@ template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF, int A
 __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, TileCoord tc,
                                           int e, int row0) {
   using C = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
-  static_assert(AV == 0 || (WF == 0 && S >= 3), "split ring: bf16, B ring of >= 3");
+  static_assert(AV == 0 || S >= 3, "split ring: B ring of 3 or more");
   using BT = typename std::conditional<WF == 1, uint8_t, uint16_t>::type;
   static_assert(WF == 0 || MODE < 2, "e4m3 weights are for the expert GEMMs");
   const bool shared = MODE != 2 && e == a.E;

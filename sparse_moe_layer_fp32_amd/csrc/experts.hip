@@ -30,7 +30,7 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   }
   if constexpr (WF == 1) {
     if (e == a.E) {  // shared expert: bf16 weights
-      gemm_tile<MODE, BM, BN, BK, WM, WN, S, 0>(a, smem, tc, e, row0);
+      gemm_tile<MODE, BM, BN, BK, WM, WN, S, 0, AV>(a, smem, tc, e, row0);
       return;
     }
   }
@@ -83,7 +83,8 @@ int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape) {
 // Tile shapes.  Big (many rows per expert): 256 x 256, k step 64 (128-byte
 // row pieces), 8 waves of 128 x 64 (two per SIMD, so one wave's stalls are
 // covered by the other's MFMAs), split ring with A 2-deep and B 3-deep, the
-// whole 160 KB of LDS; the e4m3 launches keep k step 32 and a 4-deep ring.
+// whole 160 KB of LDS (e4m3 launches too: their B stages are half the size,
+// and the shared expert's bf16 tiles in them take the same ring).
 // Small (few rows per expert, the GEMMs stream weights): 64 rows, 3-deep
 // ring, one block per CU; gate/up 64 h columns (128 weight rows) with k step
 // 128, so every weight row is read in 256-byte pieces; down 256 output
@@ -94,7 +95,8 @@ hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipS
   const int maxn = std::max(a.I, a.Is);
   if (fp8) {
     if (shape == kTileBig)
-      return launch_one<0, 256, 256, 32, 2, 4, 4, 1>(a, tile_capacity, (maxn + 127) / 128, stream);
+      return launch_one<0, 256, 256, 64, 2, 4, 3, 1, 1>(a, tile_capacity, (maxn + 127) / 128,
+                                                        stream);
     return launch_one<0, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, (maxn + 63) / 64, stream);
   }
   if (shape == kTileBig)
@@ -107,7 +109,7 @@ hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStr
                        int fp8) {
   if (fp8) {
     if (shape == kTileBig)
-      return launch_one<1, 256, 256, 32, 2, 4, 4, 1>(a, tile_capacity, a.H / 256, stream);
+      return launch_one<1, 256, 256, 64, 2, 4, 3, 1, 1>(a, tile_capacity, a.H / 256, stream);
     return launch_one<1, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, a.H / 128, stream);
   }
   if (shape == kTileBig)
@@ -118,10 +120,11 @@ hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStr
 }
 
 hipError_t launch_router_logits(const ExpertArgs& a, hipStream_t stream) {
-  // Enough 256-row tiles to fill the GPU: 8 waves of 64 x 64; else 64 x 128.
+  // Enough 256-row tiles to fill the GPU: 8 waves of 64 x 64, split ring at
+  // k step 64; else 64 x 128.
   if (a.T >= 8192)
-    return launch_one<2, 256, 128, 32, 4, 2, 4>(a, static_cast<int>((a.T + 255) / 256),
-                                               a.Np / 128, stream);
+    return launch_one<2, 256, 128, 64, 4, 2, 3, 0, 1>(a, static_cast<int>((a.T + 255) / 256),
+                                                     a.Np / 128, stream);
   return launch_one<2, 64, 128, 64, 2, 2, 3>(a, static_cast<int>((a.T + 63) / 64), a.Np / 128,
                                              stream);
 }
