@@ -75,6 +75,30 @@ __device__ __forceinline__ TileCoord tile_of(int u, int ntiles, int NT) {
   return {first + within % gm, within / gm};
 }
 
+// Scheduling groups that follow the experts: the tile list holds each
+// expert's row tiles consecutively and in row order, so the tiles of one
+// expert are cut into groups of at most GROUP_M, and unit u's group is
+// found from the tile u / NT (a group of gm tiles owns the gm NT units from
+// its first tile times NT on).  Inside a group the row tile runs fastest,
+// so blocks running together share the expert's weight column tiles and
+// each row tile's activations; a group never mixes experts, whose weight
+// tiles nothing would share.
+template <int BM>
+__device__ __forceinline__ TileCoord tile_of_expert(int u, int NT, const int2* tiles,
+                                                    const int32_t* offsets, int E, int64_t T) {
+  const int t = u / NT;
+  const int2 tile = tiles[t];
+  const bool shared = tile.x == E;
+  const int base = shared ? 0 : offsets[tile.x];
+  const int64_t n = shared ? T : offsets[tile.x + 1] - base;
+  const int i = (tile.y - base) / BM;  // the tile's index among its expert's
+  const int gi = i / GROUP_M * GROUP_M;
+  const int first = t - (i - gi);
+  const int gm = static_cast<int>(min<int64_t>(GROUP_M, (n + BM - 1) / BM - gi));
+  const int within = u - first * NT;
+  return {first + within % gm, within / gm};
+}
+
 // AV = 1 (split ring): A goes through its own 2-deep LDS ring, one k step
 // ahead; B through an S-deep ring, S-1 steps ahead.
 template <int BM, int BN, int BK, int WM, int WN, int S, int WF = 0, int AV = 0>
@@ -131,7 +155,13 @@ struct Cfg {
 // row's scale in the epilogue (a scale per output row factors out of the
 // dot product).  The shared expert's tiles (bf16 weights) in such a launch
 // take the bf16 body: the choice is made once per block.
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF, int AV = 0>
+//
+// STAGED (down only): the output tile leaves through LDS in whole rows, and
+// waves without rows end before the epilogue's barriers, so the caller
+// ends the block after the tile.  A persistent caller, whose waves go on to
+// other work, passes false: direct stores, no barrier after the mainloop.
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF, int AV = 0,
+          bool STAGED = true>
 __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, TileCoord tc,
                                           int e, int row0) {
   using C = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
@@ -546,10 +576,30 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
   // ---- epilogue.  The MFMAs take the weight rows as their first operand,
   // so acc[mb][nb] holds the transposed block: lane l owns token row
   // 32 mb + (l % 32) of the wave's rows and, for r = 4g .. 4g+3, the four
-  // consecutive output columns 8g + 4(l / 32) + 0..3 of block nb.  Each
-  // group of four goes out as one 8-byte store.
+  // consecutive output columns 8g + 4(l / 32) + 0..3 of block nb.
   const int row = wm * (BM / WM) + fr;  // + 32 mb
+  if (MODE == 2) {
+    // fp32 logits, one 16-byte store per group of four
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      if (row + 32 * mb >= rows) continue;
+      float* zrow = a.zout + static_cast<int64_t>(row0 + row + 32 * mb) * a.Np + n0 +
+                    wn * (BN / WN) + 4 * fh;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& v = acc[mb][nb];
+          *reinterpret_cast<f32x4*>(zrow + 32 * nb + 8 * g) =
+              f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+        }
+    }
+    return;
+  }
   if (MODE == 0) {
+    // h after SwiGLU, one 8-byte store per group of four (the SwiGLU work
+    // overlaps these stores across waves; staging them costs more than
+    // it saves here)
     uint16_t* out = shared ? a.h_shared : a.h_routed;
     const float lim = shared ? a.limit_shared : a.limit;
     const int half = C::NB / 2;
@@ -589,32 +639,30 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
               make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
     }
-  } else if (MODE == 2) {
+    return;
+  }
+  // Down: o = the sums times the gating weight, then the weight scale for
+  // e4m3.
+  f32x4 sd[C::NB][4];
+  if constexpr (WF == 1) {
+    const float* sdp = a.s_down + static_cast<int64_t>(e) * H + n0 + wn * (BN / WN) + 4 * fh;
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
-      if (row + 32 * mb >= rows) continue;
-      float* zrow = a.zout + static_cast<int64_t>(row0 + row + 32 * mb) * a.Np + n0 +
-                    wn * (BN / WN) + 4 * fh;
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
+      for (int g = 0; g < 4; ++g) sd[nb][g] = *reinterpret_cast<const f32x4*>(sdp + 32 * nb + 8 * g);
+  }
+  auto o4 = [&](int mb, int nb, int g) {
+    const f32x16& v = acc[mb][nb];
+    float o[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16& v = acc[mb][nb];
-          *reinterpret_cast<f32x4*>(zrow + 32 * nb + 8 * g) =
-              f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
-        }
+    for (int q = 0; q < 4; ++q) {
+      o[q] = v[4 * g + q] * wt[mb];
+      if constexpr (WF == 1) o[q] *= sd[nb][g][q];
     }
-  } else {
-    uint16_t* out = shared ? a.o_shared : a.o_routed;
-    // e4m3 weights: the scales of this lane's output rows (columns of o)
-    f32x4 sd[C::NB][4];
-    if constexpr (WF == 1) {
-      const float* sdp = a.s_down + static_cast<int64_t>(e) * H + n0 + wn * (BN / WN) + 4 * fh;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) sd[nb][g] = *reinterpret_cast<const f32x4*>(sdp + 32 * nb + 8 * g);
-    }
+    return make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+  };
+  uint16_t* out = shared ? a.o_shared : a.o_routed;
+  if constexpr (!STAGED) {
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
       if (row + 32 * mb >= rows) continue;
@@ -623,18 +671,45 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16& v = acc[mb][nb];
-          float o[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            o[q] = v[4 * g + q] * wt[mb];
-            if constexpr (WF == 1) o[q] *= sd[nb][g][q];
-          }
-          *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * g) =
-              make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-        }
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * g) = o4(mb, nb, g);
     }
+    return;
+  }
+  // STAGED: the bf16 tile goes through LDS, free now (no DMA in flight;
+  // the barrier below has every wave past its last fragment read), row by
+  // row with the 16-byte chunks of row r XOR-rotated by r so the 32 rows of
+  // one write instruction land in different banks, then leaves as whole
+  // rows: each thread moves 16 bytes, eight threads a 128-byte line.
+  // Stored one group of four per lane instead, every store instruction
+  // touches 32 rows 2H bytes apart.  Waves without rows have ended here
+  // (a barrier waits for the surviving waves only), so the rows are copied
+  // out by the waves holding them: those of the first ceil(rows / (BM/WM))
+  // wave rows.
+  constexpr int OCH = BN / 8;  // 16-byte chunks per staged row
+  static_assert((OCH & (OCH - 1)) == 0 && OCH >= 4, "power-of-two chunks per row");
+  static_assert(BM * BN * 2 <= Cfg<BM, BN, BK, WM, WN, S, 0, AV>::LDS_BYTES,
+                "the output tile fits the LDS");
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int r = row + 32 * mb;
+    if (r >= rows) continue;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = wn * (BN / WN) + 32 * nb + 8 * g + 4 * fh;  // first of the four columns
+        *reinterpret_cast<uint2*>(smem + (r * OCH + ((c >> 3) ^ (r & (OCH - 1)))) * 16 +
+                                  (c & 4) * 2) = o4(mb, nb, g);
+      }
+  }
+  __syncthreads();
+  const int alive = min(WM, (rows + BM / WM - 1) / (BM / WM)) * WN * 64;
+#pragma unroll 4
+  for (int i = tid; i < rows * OCH; i += alive) {
+    const int r = i / OCH, c = i % OCH;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + (r * OCH + (c ^ (r & (OCH - 1)))) * 16);
+    *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row0 + r) * H + n0 + c * 8) = v;
   }
 }
 

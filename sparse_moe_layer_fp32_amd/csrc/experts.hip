@@ -18,7 +18,8 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   const int ntiles = MODE == 2 ? static_cast<int>((a.T + BM - 1) / BM) : *a.ntiles;
   const int u = xcd_remap(blockIdx.x, ntiles * a.NT);
   if (u < 0) return;
-  const TileCoord tc = tile_of(u, ntiles, a.NT);
+  const TileCoord tc = MODE == 2 ? tile_of(u, ntiles, a.NT)
+                                 : tile_of_expert<BM>(u, a.NT, a.tiles, a.offsets, a.E, a.T);
   int e, row0;
   if (MODE == 2) {
     e = 0;

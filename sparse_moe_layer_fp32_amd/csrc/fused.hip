@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(FusedArgs f) {
       case kPhSharedDown: {
         const int j = t / s.ntd;
         if (block_wait(ctl, kCtlSharedGu + j, s.ntg_s, kStSharedGu, &s_ctl[3]))
-          gemm_tile<1, 64, 128, 64, 2, 2, 3, 0>(f.g, smem, TileCoord{0, t % s.ntd}, E, 64 * j);
+          gemm_tile<1, 64, 128, 64, 2, 2, 3, 0, 0, false>(f.g, smem, TileCoord{0, t % s.ntd}, E, 64 * j);
         block_signal(ctl, kCtlDownDone);
         break;
       }
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(FusedArgs f) {
         if (block_wait(ctl, kCtlTileGu + i, s.ntg, kStGu, &s_ctl[3])) {
           const int2 tile = f.tiles[i];
           if (tile_ok(tile, E, s.P))
-            gemm_tile<1, 64, 128, 64, 2, 2, 3, 0>(f.g, smem, TileCoord{0, t % s.ntd}, tile.x,
+            gemm_tile<1, 64, 128, 64, 2, 2, 3, 0, 0, false>(f.g, smem, TileCoord{0, t % s.ntd}, tile.x,
                                                   tile.y);
         }
         block_signal(ctl, kCtlDownDone);
