@@ -13,6 +13,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, blocks are dealt round-robin
+// s_getreg_b32 operand for HW_REG_XCC_ID (register 20, bits 3:0): the XCD
+// the wave runs on.
+constexpr int kHwRegXccId = 20 | (3 << 11);
 
 // ------------------------------------------------------------------ bf16
 

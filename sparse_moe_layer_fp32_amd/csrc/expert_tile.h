@@ -160,12 +160,17 @@ struct Cfg {
 // waves without rows end before the epilogue's barriers, so the caller
 // ends the block after the tile.  A persistent caller, whose waves go on to
 // other work, passes false: direct stores, no barrier after the mainloop.
+//
+// JOIN (split ring, staged down only): waves without rows do not end after
+// the mainloop but pass the epilogue's barriers and help store, for a
+// persistent caller whose waves all go on to the next tile.
 template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF, int AV = 0,
-          bool STAGED = true>
+          bool STAGED = true, bool JOIN = false>
 __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, TileCoord tc,
                                           int e, int row0) {
   using C = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
   static_assert(AV == 0 || S >= 3, "split ring: B ring of 3 or more");
+  static_assert(!JOIN || (AV && MODE == 1 && STAGED), "JOIN: split-ring staged down tiles");
   using BT = typename std::conditional<WF == 1, uint8_t, uint16_t>::type;
   static_assert(WF == 0 || MODE < 2, "e4m3 weights are for the expert GEMMs");
   const bool shared = MODE != 2 && e == a.E;
@@ -396,7 +401,7 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
           for (int j = 0; j < C::JB; ++j) b_issue(kt + S - 1, j);
         if (kt + 1 < KT) step_end(kt);
       }
-      return;
+      if constexpr (!JOIN) return;
     }
     auto step = [&](int kt, auto REFILL) {
       constexpr bool refill = decltype(REFILL)::value;
@@ -417,9 +422,11 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
         for (int j = MFMAS / DMA_EVERY; j < C::JB; ++j) b_issue(kt + S - 1, j);
       if (kt + 1 < KT) step_end(kt);
     };
-    int kt = 0;
-    for (; kt + S - 1 < KT; ++kt) step(kt, std::true_type{});
-    for (; kt < KT; ++kt) step(kt, std::false_type{});
+    if (!JOIN || has_rows) {
+      int kt = 0;
+      for (; kt + S - 1 < KT; ++kt) step(kt, std::true_type{});
+      for (; kt < KT; ++kt) step(kt, std::false_type{});
+    }
   } else if constexpr (S >= 4) {
     // Ring of S >= 4 buffers, two stages in flight.  Step kt: refill stage
     // kt+2 (buffer of stage kt-2) during the first half of stage kt's MFMAs;
@@ -571,7 +578,7 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
     for (; kt + S - 1 < KT; ++kt) step(kt, std::true_type{});
     for (; kt < KT; ++kt) step(kt, std::false_type{});
   }
-  if (!has_rows) return;
+  if (!JOIN && !has_rows) return;
 
   // ---- epilogue.  The MFMAs take the weight rows as their first operand,
   // so acc[mb][nb] holds the transposed block: lane l owns token row
@@ -681,10 +688,11 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
   // one write instruction land in different banks, then leaves as whole
   // rows: each thread moves 16 bytes, eight threads a 128-byte line.
   // Stored one group of four per lane instead, every store instruction
-  // touches 32 rows 2H bytes apart.  Waves without rows have ended here
-  // (a barrier waits for the surviving waves only), so the rows are copied
-  // out by the waves holding them: those of the first ceil(rows / (BM/WM))
-  // wave rows.
+  // touches 32 rows 2H bytes apart.  Without JOIN, waves without rows have
+  // ended here (a barrier waits for the surviving waves only), so the rows
+  // are copied out by the waves holding them: those of the first
+  // ceil(rows / (BM/WM)) wave rows.  With JOIN every wave is here (the
+  // staging loop below skips rows past the group's end).
   constexpr int OCH = BN / 8;  // 16-byte chunks per staged row
   static_assert((OCH & (OCH - 1)) == 0 && OCH >= 4, "power-of-two chunks per row");
   static_assert(BM * BN * 2 <= Cfg<BM, BN, BK, WM, WN, S, 0, AV>::LDS_BYTES,
@@ -704,7 +712,7 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
       }
   }
   __syncthreads();
-  const int alive = min(WM, (rows + BM / WM - 1) / (BM / WM)) * WN * 64;
+  const int alive = JOIN ? C::THREADS : min(WM, (rows + BM / WM - 1) / (BM / WM)) * WN * 64;
 #pragma unroll 4
   for (int i = tid; i < rows * OCH; i += alive) {
     const int r = i / OCH, c = i % OCH;

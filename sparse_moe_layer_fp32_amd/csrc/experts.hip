@@ -38,6 +38,80 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   gemm_tile<MODE, BM, BN, BK, WM, WN, S, WF, AV>(a, smem, tc, e, row0);
 }
 
+// Barrier that orders LDS accesses only (a full __syncthreads also waits
+// for the wave's global stores).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Persistent form of the big tiles: one block per CU takes units (row tile,
+// column tile) from its own XCD's queue, the XCD's contiguous share of the
+// units in schedule order, and once that is empty from the other XCDs'
+// queues, so the XCDs finish together whatever their speeds.  queue[x] is
+// XCD x's counter, zero at launch; a block requests its next unit's ticket
+// before starting the current tile, so the round trip overlaps the tile.
+// No block waits for another.
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF, int AV>
+__global__ __launch_bounds__(64 * WM * WN) void expert_gemm_persistent(ExpertArgs a,
+                                                                        uint32_t* queue) {
+  using C0 = Cfg<BM, BN, BK, WM, WN, S, 0, AV>;
+  using C1 = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
+  constexpr int LDS = C0::LDS_BYTES > C1::LDS_BYTES ? C0::LDS_BYTES : C1::LDS_BYTES;
+  constexpr bool JOIN = MODE == 1;  // the staged down epilogue has barriers
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+  // The unit is handed to the block's waves in the LDS's last word: the last
+  // weight-ring slot, which no DMA writes before the tile's first k step
+  // (after the prologue barrier, by when every wave has read it), and which
+  // neither epilogue uses.
+  static_assert(S >= 3 && AV == 1 && LDS == C0::LDS_BYTES,
+                "split ring: the LDS ends with the last bf16 B slot, free until step 0");
+  static_assert(kQueueWords == 2 * kNumXcd, "a queue per XCD and GEMM");
+  static_assert(BM * BN * 2 <= LDS - 4, "the staged down tile stays clear of it");
+  int& s_unit = *reinterpret_cast<int*>(smem + LDS - 4);
+
+  const int total = *a.ntiles * a.NT;
+  const int per = (total + kNumXcd - 1) / kNumXcd;
+  const int xcc = static_cast<int>(__builtin_amdgcn_s_getreg(kHwRegXccId)) & (kNumXcd - 1);
+  auto len_of = [&](int y) { return max(0, min(per, total - y * per)); };
+  auto take = [&](int y) {
+    const uint32_t t =
+        __hip_atomic_fetch_add(queue + y, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return t < static_cast<uint32_t>(len_of(y)) ? y * per + static_cast<int>(t) : -1;
+  };
+  auto steal = [&] {
+    for (int j = 1; j < kNumXcd; ++j) {
+      const int y = (xcc + j) & (kNumXcd - 1);
+      if (__hip_atomic_load(queue + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+          static_cast<uint32_t>(len_of(y)))
+        continue;
+      const int u = take(y);
+      if (u >= 0) return u;
+    }
+    return -1;
+  };
+  if (threadIdx.x == 0) {
+    const int u = take(xcc);
+    s_unit = u >= 0 ? u : steal();
+  }
+  __syncthreads();
+  int u = s_unit;
+  while (u >= 0) {
+    int next = -1;
+    if (threadIdx.x == 0) next = take(xcc);
+    const TileCoord tc = tile_of_expert<BM>(u, a.NT, a.tiles, a.offsets, a.E, a.T);
+    const int2 tile = a.tiles[tc.mt];
+    if (WF == 1 && tile.x == a.E)  // shared expert: bf16 weights
+      gemm_tile<MODE, BM, BN, BK, WM, WN, S, 0, AV, true, JOIN>(a, smem, tc, tile.x, tile.y);
+    else
+      gemm_tile<MODE, BM, BN, BK, WM, WN, S, WF, AV, true, JOIN>(a, smem, tc, tile.x, tile.y);
+    // LDS-only barriers: the tile's global stores drain on their own.
+    lds_barrier();  // every wave is past the tile's last LDS access
+    if (threadIdx.x == 0) s_unit = next >= 0 ? next : steal();
+    lds_barrier();
+    u = s_unit;
+  }
+}
+
 // One thread per 8 consecutive outputs (combine_row).
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o_routed,
                                                       const uint16_t* __restrict__ o_shared,
@@ -58,6 +132,20 @@ hipError_t launch_one(const ExpertArgs& a, int tile_capacity, int NT, hipStream_
   b.NT = NT;
   expert_gemm<MODE, BM, BN, BK, WM, WN, S, WF, AV>
       <<<static_cast<unsigned>(grid), C::THREADS, 0, stream>>>(b);
+  return hipGetLastError();
+}
+
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF, int AV>
+hipError_t launch_persistent(const ExpertArgs& a, int NT, uint32_t* queue, hipStream_t stream) {
+  using C = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  ExpertArgs b = a;
+  b.NT = NT;
+  expert_gemm_persistent<MODE, BM, BN, BK, WM, WN, S, WF, AV>
+      <<<static_cast<unsigned>(std::max(cus, 1)), C::THREADS, 0, stream>>>(b, queue);
   return hipGetLastError();
 }
 
@@ -96,13 +184,13 @@ hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipS
   const int maxn = std::max(a.I, a.Is);
   if (fp8) {
     if (shape == kTileBig)
-      return launch_one<0, 256, 256, 64, 2, 4, 3, 1, 1>(a, tile_capacity, (maxn + 127) / 128,
-                                                        stream);
+      return launch_persistent<0, 256, 256, 64, 2, 4, 3, 1, 1>(a, (maxn + 127) / 128, a.queue,
+                                                               stream);
     return launch_one<0, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, (maxn + 63) / 64, stream);
   }
   if (shape == kTileBig)
-    return launch_one<0, 256, 256, 64, 2, 4, 3, 0, 1>(a, tile_capacity, (maxn + 127) / 128,
-                                                      stream);
+    return launch_persistent<0, 256, 256, 64, 2, 4, 3, 0, 1>(a, (maxn + 127) / 128, a.queue,
+                                                             stream);
   return launch_one<0, 64, 128, 128, 2, 2, 3>(a, tile_capacity, (maxn + 63) / 64, stream);
 }
 
@@ -110,11 +198,13 @@ hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStr
                        int fp8) {
   if (fp8) {
     if (shape == kTileBig)
-      return launch_one<1, 256, 256, 64, 2, 4, 3, 1, 1>(a, tile_capacity, a.H / 256, stream);
+      return launch_persistent<1, 256, 256, 64, 2, 4, 3, 1, 1>(a, a.H / 256, a.queue + kNumXcd,
+                                                               stream);
     return launch_one<1, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, a.H / 128, stream);
   }
   if (shape == kTileBig)
-    return launch_one<1, 256, 256, 64, 2, 4, 3, 0, 1>(a, tile_capacity, a.H / 256, stream);
+    return launch_persistent<1, 256, 256, 64, 2, 4, 3, 0, 1>(a, a.H / 256, a.queue + kNumXcd,
+                                                             stream);
   if (a.H % 256 == 0)
     return launch_one<1, 64, 256, 64, 2, 4, 3>(a, tile_capacity, a.H / 256, stream);
   return launch_one<1, 64, 128, 64, 2, 2, 3>(a, tile_capacity, a.H / 128, stream);

@@ -11,6 +11,9 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kTopkBlockTokens = 2048;  // below: one top-k block per token
+// Queue counters of the persistent big-tile GEMMs: one per XCD for gate/up,
+// then one per XCD for down; the tile-list writer zeroes them.
+constexpr int kQueueWords = 16;
 
 // Where the router's partial logits live: partial s of logit (t, e) is
 // zpart[t ld + e es + s ps], summed over s = 0 .. S-1 in order.
@@ -42,6 +45,7 @@ struct ExpertArgs {
   uint16_t* o_routed;       // [P][H]
   uint16_t* o_shared;       // [T][H]
   int NT;                   // column tiles (set by the launcher)
+  uint32_t* queue;          // kQueueWords work-queue counters (persistent big tiles)
   // FP8 routed experts (when the launch says so): e4m3 codes in the layouts of
   // w_gate/w_up/w_down and one fp32 scale per output row.
   const uint8_t* w8_gate;   // [E][I][H]
@@ -126,15 +130,16 @@ hipError_t launch_topk(const float* zpart, PartialLayout pl, const float* bias, 
                        hipStream_t stream);
 
 // permute.hip; ev (optional) receives three events, one before each kernel.
+// queue (may be null): kQueueWords counters zeroed with the tile list.
 hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, int with_shared,
                           int32_t* rank, int32_t* hist, int32_t* base, int32_t* offsets,
                           int32_t* sorted, int32_t* pos, int2* tiles, int32_t* ntiles,
-                          const float* topk_w, float* w_sorted, hipStream_t stream,
-                          hipEvent_t* ev);
+                          uint32_t* queue, const float* topk_w, float* w_sorted,
+                          hipStream_t stream, hipEvent_t* ev);
 
 hipError_t launch_fill_zero(int32_t* p, int n, hipStream_t stream);
-hipError_t launch_dense_tiles(int2* tiles, int32_t* ntiles, int64_t T, int bm, int group,
-                              hipStream_t stream);
+hipError_t launch_dense_tiles(int2* tiles, int32_t* ntiles, uint32_t* queue, int64_t T, int bm,
+                              int group, hipStream_t stream);
 int permute_chunk(int P);        // pairs per rank/histogram chunk (at most 64 chunks)
 int permute_hist_stride(int P);  // histogram row stride: chunk count rounded up to 4
 

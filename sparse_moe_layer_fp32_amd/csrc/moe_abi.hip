@@ -42,8 +42,8 @@ struct Plan {
   int C;         // permutation chunks, padded to a multiple of 4
   int shape;     // expert GEMM tile shape (kTileBig / kTileSmall)
   int tile_cap;  // capacity of the GEMM tile list
-  size_t zpart, wsplit, ids, w, rank, hist, base, offsets, sorted, pos, wsorted, tiles, ntiles, h,
-      o, ctl, total;
+  size_t zpart, wsplit, ids, w, rank, hist, base, offsets, sorted, pos, wsorted, tiles, ntiles,
+      queue, h, o, ctl, total;
 };
 
 moe_status validate(const moe_config* c) {
@@ -112,6 +112,7 @@ void make_plan(const moe_config* c, Plan* p) {
   p->wsorted = take(P * 4);
   p->tiles = take(static_cast<size_t>(p->tile_cap) * 8);
   p->ntiles = take(16);
+  p->queue = take(moe::kQueueWords * 4);
   p->h = take((P * p->I + T64 * p->Is) * 2);
   p->o = take((P + (p->Is > 0 ? T64 : 0)) * p->H * 2);
   p->total = off;
@@ -186,7 +187,8 @@ moe_status permute_impl(const Plan& p, const int32_t* ids, int32_t* offsets, int
       moe::launch_permute(ids, static_cast<int>(p.P), p.E, p.T, moe::experts_tile_rows(p.shape),
                           p.Is > 0, at<int32_t>(ws, p.rank), at<int32_t>(ws, p.hist),
                           at<int32_t>(ws, p.base), offsets, sorted, pos, at<int2>(ws, p.tiles),
-                          at<int32_t>(ws, p.ntiles), w, w ? at<float>(ws, p.wsorted) : nullptr,
+                          at<int32_t>(ws, p.ntiles), at<uint32_t>(ws, p.queue), w,
+                          w ? at<float>(ws, p.wsorted) : nullptr,
                           stream, ev),
       "permute");
   return MOE_OK;
@@ -220,6 +222,7 @@ moe::ExpertArgs expert_args(const Plan& p, const moe_config* c, const uint16_t* 
   g.tiles = at<int2>(ws, p.tiles);
   g.ntiles = at<int32_t>(ws, p.ntiles);
   g.offsets = at<int32_t>(ws, p.offsets);
+  g.queue = at<uint32_t>(ws, p.queue);
   g.h_routed = h_routed;
   g.h_shared = h_routed + static_cast<size_t>(p.P) * p.I;
   g.o_routed = o_routed;
@@ -356,7 +359,7 @@ struct DensePlan {
   int64_t T;
   int H, I;
   int shape, tile_cap;
-  size_t tiles, ntiles, h, total;
+  size_t tiles, ntiles, queue, h, total;
 };
 
 moe_status validate_dense(const moe_dense_config* c) {
@@ -390,6 +393,7 @@ void make_dense_plan(const moe_dense_config* c, DensePlan* p) {
   };
   p->tiles = take(static_cast<size_t>(p->tile_cap) * 8);
   p->ntiles = take(16);
+  p->queue = take(moe::kQueueWords * 4);
   p->h = take(static_cast<size_t>(p->T) * p->I * 2);
   p->total = off;
 }
@@ -440,10 +444,12 @@ moe_status moe_dense_forward(const moe_dense_config* cfg, const uint16_t* x,
   g.limit_shared = cfg->swiglu_limit;
   g.tiles = at<int2>(ws, p.tiles);
   g.ntiles = at<int32_t>(ws, p.ntiles);
+  g.queue = at<uint32_t>(ws, p.queue);
   g.h_shared = at<uint16_t>(ws, p.h);
   g.o_shared = y;
-  MOE_CHECK_LAUNCH(moe::launch_dense_tiles(at<int2>(ws, p.tiles), at<int32_t>(ws, p.ntiles), p.T,
-                                           moe::experts_tile_rows(p.shape), 0, stream),
+  MOE_CHECK_LAUNCH(moe::launch_dense_tiles(at<int2>(ws, p.tiles), at<int32_t>(ws, p.ntiles),
+                                           g.queue, p.T, moe::experts_tile_rows(p.shape), 0,
+                                           stream),
                    "dense tile list");
   MOE_CHECK_LAUNCH(moe::launch_gateup(g, p.shape, p.tile_cap, stream), "dense gate/up gemm");
   MOE_CHECK_LAUNCH(moe::launch_down(g, p.shape, p.tile_cap, stream), "dense down gemm");

@@ -62,9 +62,10 @@ __device__ int block_excl_scan(int v, int* smem, int* total) {
 
 // Offsets from per-expert counts (one per thread, experts 0..E-1), then the
 // tile list: routed tiles expert by expert, then the shared expert's.
+// queue (may be null): the big-tile GEMMs' work-queue counters, zeroed here.
 __device__ void offsets_and_tiles(int count, int E, int64_t T, int bm, int with_shared,
                                   int* smem, int32_t* offsets, int32_t* offs_lds,
-                                  int2* tiles, int32_t* ntiles) {
+                                  int2* tiles, int32_t* ntiles, uint32_t* queue) {
   const int tid = threadIdx.x;
   int tot = 0;
   const int off = block_excl_scan(tid < E ? count : 0, smem, &tot);
@@ -80,6 +81,7 @@ __device__ void offsets_and_tiles(int count, int E, int64_t T, int bm, int with_
   const int nshared = with_shared ? static_cast<int>((T + bm - 1) / bm) : 0;
   for (int i = tid; i < nshared; i += 1024) tiles[ntot + i] = make_int2(E, i * bm);
   if (tid == 0) *ntiles = ntot + nshared;
+  if (queue && tid < kQueueWords) queue[tid] = 0u;
 }
 
 // Ranks of the n <= kSmallPairs pairs staged in sid[0..n) among the earlier
@@ -119,8 +121,8 @@ __device__ void block_rank(const int32_t* sid, int n, int E, int nbits,
 __global__ __launch_bounds__(1024) void permute_small_kernel(
     const int32_t* __restrict__ ids, int P, int E, int64_t T, int bm, int with_shared,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
-    int2* __restrict__ tiles, int32_t* __restrict__ ntiles, const float* __restrict__ topk_w,
-    float* __restrict__ w_sorted) {
+    int2* __restrict__ tiles, int32_t* __restrict__ ntiles, uint32_t* __restrict__ queue,
+    const float* __restrict__ topk_w, float* __restrict__ w_sorted) {
   __shared__ int32_t sid[kSmallPairs];
   __shared__ int32_t srank[kSmallPairs];
   __shared__ int32_t wcnt[16][kMaxExperts];
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   __syncthreads();
   block_rank(sid, P, E, id_bits(E), wcnt, run, srank);
   const int count = tid < E ? run[tid] : 0;
-  offsets_and_tiles(count, E, T, bm, with_shared, smem, offsets, run, tiles, ntiles);
+  offsets_and_tiles(count, E, T, bm, with_shared, smem, offsets, run, tiles, ntiles, queue);
   __syncthreads();
   for (int p = tid; p < P; p += 1024) {
     const int e = sid[p];
@@ -189,7 +191,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ base,
                                                     int32_t* __restrict__ offsets,
                                                     int2* __restrict__ tiles,
-                                                    int32_t* __restrict__ ntiles) {
+                                                    int32_t* __restrict__ ntiles,
+                                                    uint32_t* __restrict__ queue) {
   __shared__ int smem[40];
   const int e = threadIdx.x;
   int count = 0;
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
       }
     }
   }
-  offsets_and_tiles(count, E, T, bm, with_shared, smem, offsets, nullptr, tiles, ntiles);
+  offsets_and_tiles(count, E, T, bm, with_shared, smem, offsets, nullptr, tiles, ntiles, queue);
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids,
@@ -243,11 +246,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 }
 
 // Tile list of a single group of T rows (the dense FFN): (group, first row).
-__global__ void dense_tiles_kernel(int2* __restrict__ tiles, int32_t* __restrict__ ntiles, int n,
-                                   int bm, int group) {
+__global__ void dense_tiles_kernel(int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                   uint32_t* __restrict__ queue, int n, int bm, int group) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) tiles[i] = make_int2(group, i * bm);
   if (i == 0) *ntiles = n;
+  if (queue && i < kQueueWords) queue[i] = 0u;
 }
 
 __global__ void fill_zero_kernel(int32_t* __restrict__ p, int n) {
@@ -269,10 +273,12 @@ int permute_chunk(int P) {
   return std::max(kSmallPairs, (per + kSmallPairs - 1) / kSmallPairs * kSmallPairs);
 }
 
-hipError_t launch_dense_tiles(int2* tiles, int32_t* ntiles, int64_t T, int bm, int group,
-                              hipStream_t stream) {
+hipError_t launch_dense_tiles(int2* tiles, int32_t* ntiles, uint32_t* queue, int64_t T, int bm,
+                              int group, hipStream_t stream) {
   const int n = static_cast<int>((T + bm - 1) / bm);
-  dense_tiles_kernel<<<(std::max(n, 1) + 255) / 256, 256, 0, stream>>>(tiles, ntiles, n, bm, group);
+  const int threads = std::max(n, kQueueWords);
+  dense_tiles_kernel<<<(threads + 255) / 256, 256, 0, stream>>>(tiles, ntiles, queue, n, bm,
+                                                                group);
   return hipGetLastError();
 }
 
@@ -285,12 +291,12 @@ hipError_t launch_fill_zero(int32_t* p, int n, hipStream_t stream) {
 hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, int with_shared,
                           int32_t* rank, int32_t* hist, int32_t* base, int32_t* offsets,
                           int32_t* sorted, int32_t* pos, int2* tiles, int32_t* ntiles,
-                          const float* topk_w, float* w_sorted, hipStream_t stream,
-                          hipEvent_t* ev) {
+                          uint32_t* queue, const float* topk_w, float* w_sorted,
+                          hipStream_t stream, hipEvent_t* ev) {
   if (P <= kSmallPairs) {
     if (ev) hipEventRecord(ev[0], stream);
     permute_small_kernel<<<1, 1024, 0, stream>>>(ids, P, E, T, bm, with_shared, offsets, sorted,
-                                                 pos, tiles, ntiles, topk_w, w_sorted);
+                                                 pos, tiles, ntiles, queue, topk_w, w_sorted);
     if (ev) {
       hipEventRecord(ev[1], stream);
       hipEventRecord(ev[2], stream);
@@ -306,7 +312,7 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int64_t T, int bm, i
   if (err != hipSuccess) return err;
   if (ev) hipEventRecord(ev[1], stream);
   scan_kernel<<<1, 1024, 0, stream>>>(hist, C, Cp, E, T, bm, with_shared, base, offsets, tiles,
-                                      ntiles);
+                                      ntiles, queue);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev) hipEventRecord(ev[2], stream);
