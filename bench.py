@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -161,8 +162,9 @@ def summarize_profiles(d):
             lines.append(f"| {wl} | `{_short(k)}` | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
             short = _short(k)
             base = short.split("<")[0]
-            key = ("gateup_kernel" if short.startswith("expert_gemm<0") else
-                   "down_kernel" if short.startswith("expert_gemm<1") else base)
+            mode = re.match(r"expert_gemm(?:_persistent)?<(\d)", short)
+            key = ("gateup_kernel" if mode and mode.group(1) == "0" else
+                   "down_kernel" if mode and mode.group(1) == "1" else base)
             traffic[f"{key}:{wl}"] = {"kernel": short, "read_bytes": rb, "write_bytes": wb,
                                       "bytes_per_launch": rb + wb,
                                       "source_sha256": _src_sha(KERNEL_SOURCES.get(base, _EXPERT_SRC))}
@@ -395,9 +397,9 @@ def cpu_baseline(wl, inp):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no "
-              "multi-GPU path; the layer would shard by tokens or by experts, see DESIGN.md",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): there is no "
+              "multi-GPU path; the layer would shard by tokens (each GPU a full replica) or "
+              "by experts (an all-to-all of the routed pairs)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
