@@ -51,9 +51,13 @@ typedef __attribute__((address_space(1))) const void gbl_void;
 
 constexpr int GROUP_M = 8;    // row tiles per scheduling group
 
+// CPOL is the load's cache policy: 0, or kCpolNt for data read once (the
+// non-temporal hint: the lines are the first to go from the caches).
+template <int CPOL = 0>
 __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)lds_wave_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)lds_wave_base, 16, 0, CPOL);
 }
+constexpr int kCpolNt = 2;  // gfx950 cache-policy bit NT
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -268,7 +272,12 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
       dma16(abase + aoff[d] + k0, st + (wid * C::JA + d) * 1024);
     } else {
       const int j = d - C::JA;
-      dma16(bmat + boff[j] + k0, st + BM * C::ROWB + (wid * C::JB + j) * 1024);
+      // Small expert tiles stream weights that no other block reads (few
+      // row tiles per expert): non-temporal, so they do not push the
+      // activations and outputs out of the caches (decode gate/up and down
+      // -10% each).  The router's weight planes are read by every row tile.
+      dma16<MODE == 2 ? 0 : kCpolNt>(bmat + boff[j] + k0,
+                                     st + BM * C::ROWB + (wid * C::JB + j) * 1024);
     }
   };
 
