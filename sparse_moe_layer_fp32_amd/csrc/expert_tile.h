@@ -275,9 +275,11 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
       // Small expert tiles stream weights that no other block reads (few
       // row tiles per expert): non-temporal, so they do not push the
       // activations and outputs out of the caches (decode gate/up and down
-      // -10% each).  The router's weight planes are read by every row tile.
-      dma16<MODE == 2 ? 0 : kCpolNt>(bmat + boff[j] + k0,
-                                     st + BM * C::ROWB + (wid * C::JB + j) * 1024);
+      // -10% each) -- when a k step reads whole 128-byte lines: the e4m3
+      // rows' 64-byte pieces would have each line fetched twice (+7%).  The
+      // router's weight planes are read by every row tile.
+      constexpr int bpol = (MODE != 2 && C::BROWB % 128 == 0) ? kCpolNt : 0;
+      dma16<bpol>(bmat + boff[j] + k0, st + BM * C::ROWB + (wid * C::JB + j) * 1024);
     }
   };
 
@@ -733,6 +735,10 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
 // y[t] = o_shared[t] + sum_j o[pos(t, j)] in slot order j = 0..k-1, fp32,
 // rounded once to bf16.  Thread idx computes the 8 consecutive outputs
 // 8 idx .. 8 idx + 7 of the flattened [T][H] output.
+// NT: the o rows are loaded with the non-temporal hint (large batches,
+// whose o does not stay in the caches anyway: -8% at T = 8192; decoding
+// batches' o is cache-resident and keeps the default).
+template <bool NT = false>
 __device__ __forceinline__ void combine_row(const uint16_t* __restrict__ o_routed,
                                             const uint16_t* __restrict__ o_shared,
                                             const int32_t* __restrict__ pair_pos, int k,
@@ -744,7 +750,8 @@ __device__ __forceinline__ void combine_row(const uint16_t* __restrict__ o_route
   const int d = static_cast<int>(idx - t * per_row) * 8;
   float acc[8];
   if (o_shared) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(o_shared + t * H + d);
+    const u32x4* src = reinterpret_cast<const u32x4*>(o_shared + t * H + d);
+    const u32x4 v = NT ? __builtin_nontemporal_load(src) : *src;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       acc[2 * q] = bf16_lo(v[q]);
@@ -764,7 +771,10 @@ __device__ __forceinline__ void combine_row(const uint16_t* __restrict__ o_route
     u32x4 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (pos[j] >= 0) v[j] = *reinterpret_cast<const u32x4*>(o_routed + pos[j] * H + d);
+      if (pos[j] >= 0) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(o_routed + pos[j] * H + d);
+        v[j] = NT ? __builtin_nontemporal_load(src) : *src;
+      }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (pos[j] >= 0)

@@ -113,13 +113,14 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm_persistent(ExpertArg
 }
 
 // One thread per 8 consecutive outputs (combine_row).
+template <bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o_routed,
                                                       const uint16_t* __restrict__ o_shared,
                                                       const int32_t* __restrict__ pair_pos, int k,
                                                       int64_t T, int H, int P,
                                                       uint16_t* __restrict__ y) {
-  combine_row(o_routed, o_shared, pair_pos, k, T, H, P, y,
-              static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
+  combine_row<NT>(o_routed, o_shared, pair_pos, k, T, H, P, y,
+                  static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
 }
 
 template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0, int AV = 0>
@@ -150,6 +151,9 @@ hipError_t launch_persistent(const ExpertArgs& a, int NT, uint32_t* queue, hipSt
 }
 
 }  // namespace
+
+// From this many tokens on, the combine loads o with the non-temporal hint.
+constexpr int64_t kCombineNtTokens = 1024;
 
 int experts_tile_rows(int shape) { return shape == kTileBig ? 256 : 64; }
 
@@ -226,8 +230,12 @@ hipError_t launch_combine(const uint16_t* o_routed, const uint16_t* o_shared,
   const int64_t threads = T * (H / 8);
   const int64_t blocks = (threads + 255) / 256;
   if (blocks <= 0) return hipSuccess;
-  combine_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
-      o_routed, o_shared, pair_pos, k, T, H, static_cast<int>(T * k), y);
+  if (T >= kCombineNtTokens)
+    combine_kernel<true><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
+        o_routed, o_shared, pair_pos, k, T, H, static_cast<int>(T * k), y);
+  else
+    combine_kernel<false><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
+        o_routed, o_shared, pair_pos, k, T, H, static_cast<int>(T * k), y);
   return hipGetLastError();
 }
 
