@@ -438,104 +438,6 @@ __device__ __forceinline__ void gemm_tile(const ExpertArgs& a, uint8_t* smem, Ti
       for (; kt + S - 1 < KT; ++kt) step(kt, std::true_type{});
       for (; kt < KT; ++kt) step(kt, std::false_type{});
     }
-  } else if constexpr (S >= 4) {
-    // Ring of S >= 4 buffers, two stages in flight.  Step kt: refill stage
-    // kt+2 (buffer of stage kt-2) during the first half of stage kt's MFMAs;
-    // mid-stage, wait for stage kt+1 and pass the barrier that publishes it;
-    // then read stage kt+1's first fragments while the second half of stage
-    // kt's MFMAs runs.  The barrier passed mid-stage kt-1 guarantees every
-    // wave is done with stage kt-2 before its refill.  Within a k-substep the
-    // next fragments are requested after the substep's first MFMA, so the
-    // wait before that MFMA only covers reads a whole substep old.
-    constexpr int HALF = C::KS / 2;
-    constexpr int PER_SUB = C::MB * C::NB;
-    constexpr int DMA_EVERY = (HALF * PER_SUB) / C::NI > 0 ? (HALF * PER_SUB) / C::NI : 1;
-    constexpr int DMA_IN_MFMA = (HALF * PER_SUB) / DMA_EVERY < C::NI ? (HALF * PER_SUB) / DMA_EVERY
-                                                                       : C::NI;
-    static_assert(C::KS % 2 == 0, "two halves per stage");
-    for (int s = 0; s < 2; ++s)
-      if (s < KT)
-#pragma unroll
-        for (int d = 0; d < C::NI; ++d) issue_one(s, d);
-    if (KT > 1)
-      wait_vmcnt<C::NI>();
-    else
-      wait_vmcnt<0>();
-    barrier();
-
-    // One k-substep: first MFMA, then the next fragment reads, then the rest
-    // of the MFMAs (with refill DMAs after MFMA i when dma(i) says so).
-    auto substep = [&](int set, auto next_reads, auto dma) {
-      acc[0][0] = mfma32(bf[set][0], af[set][0], acc[0][0]);
-      dma(0);
-      __builtin_amdgcn_sched_barrier(0);
-      next_reads();
-#pragma unroll
-      for (int i = 1; i < PER_SUB; ++i) {
-        const int mb = i / C::NB, nb = i % C::NB;
-        acc[mb][nb] = mfma32(bf[set][nb], af[set][mb], acc[mb][nb]);
-        dma(i);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // REFILL: stage kt+2 exists; LAST: kt is the final stage.
-    auto step = [&](int kt, auto REFILL, auto LAST) {
-      constexpr bool refill = decltype(REFILL)::value, last = decltype(LAST)::value;
-#pragma unroll
-      for (int ks = 0; ks < HALF; ++ks) {
-        substep(
-            ks & 1, [&] { load_frags(kt, ks + 1, (ks + 1) & 1); },
-            [&](int i) {
-              const int g = ks * PER_SUB + i;  // MFMA index in this half
-              if (refill && g % DMA_EVERY == DMA_EVERY - 1 && g / DMA_EVERY < DMA_IN_MFMA)
-                issue_one(kt + 2, g / DMA_EVERY);
-            });
-      }
-      if (refill)
-#pragma unroll
-        for (int d = DMA_IN_MFMA; d < C::NI; ++d) issue_one(kt + 2, d);
-      if (!last) {
-        if (refill)
-          wait_vmcnt<C::NI>();
-        else
-          wait_vmcnt<0>();
-        barrier();
-      }
-#pragma unroll
-      for (int ks = HALF; ks < C::KS; ++ks) {
-        substep(
-            ks & 1,
-            [&] {
-              if (ks + 1 < C::KS)
-                load_frags(kt, ks + 1, (ks + 1) & 1);
-              else if (!last)
-                load_frags(kt + 1, 0, 0);
-            },
-            [](int) {});
-      }
-    };
-    // Waves without rows keep the same DMA and barrier sequence.
-    auto ring_only = [&](int kt, bool refill, bool last) {
-      if (refill)
-        for (int d = 0; d < C::NI; ++d) issue_one(kt + 2, d);
-      if (!last) {
-        if (refill)
-          wait_vmcnt<C::NI>();
-        else
-          wait_vmcnt<0>();
-        barrier();
-      }
-    };
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    if (has_rows) {
-      load_frags(0, 0, 0);
-      for (int kt = 0; kt + 2 < KT; ++kt) step(kt, T_{}, F_{});
-      if (KT >= 2) step(KT - 2, F_{}, F_{});
-      step(KT - 1, F_{}, T_{});
-    } else {
-      for (int kt = 0; kt < KT; ++kt) ring_only(kt, kt + 2 < KT, kt + 1 == KT);
-    }
   } else {
     // Ring of S buffers, S-1 stages in flight: wait for stage kt, barrier
     // (all waves' DMAs of stage kt landed, all waves done with stage kt-1,
