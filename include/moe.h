@@ -81,7 +81,10 @@ typedef struct {
 
 /* Bytes of device workspace that moe_forward, moe_route and moe_permute need
  * for this configuration (one size serves all three).  Returns 0 for an
- * invalid configuration. */
+ * invalid configuration.  These three take the workspace with any contents:
+ * each call writes every word of it that it reads (work-queue counters
+ * included) before reading it, so one workspace serves calls of different
+ * batch sizes in turn (calls on it must not overlap). */
 size_t moe_workspace_size(const moe_config* cfg);
 
 /* Text of the last error on the calling thread ("" if none).  Valid until

@@ -99,6 +99,29 @@ def test_small_full_parity(moe, name):
     gu.note(f"  {name}: max err {err:.3e} M {M:.3e} near-ties {len(rep.near_tie)}")
 
 
+def test_workspace_reused_across_batch_sizes(moe):
+    """One workspace, filled with garbage once, for calls of alternating
+    batch sizes that take the big tiles (persistent grid, work queues in the
+    workspace) and the small ones: every call equals the same call on a
+    fresh workspace, bit for bit."""
+    import dataclasses
+    torch = gu.torch_mod()
+    big = synth.WORKLOADS["tiny"].with_(name="reuse", **SMALL["big_tile"])
+    d = gu.upload(synth.make_inputs(big))
+    sizes = (big.T, 48, big.T, 300, 1, big.T)
+    nbytes = max(moe.moe_workspace_size(gu.cfg_of(big, T=T)) for T in sizes)
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    for T in sizes:
+        wl = big.with_(T=T)
+        dT = dataclasses.replace(d, x=d.x[:T])
+        gu.note(f"  T={T}")
+        ref = gu.run_forward(wl, dT)
+        got = gu.run_forward(wl, dT, ws=ws)
+        assert np.array_equal(ref.ids, got.ids), f"T={T}: ids differ"
+        assert np.array_equal(ref.w.view(np.uint32), got.w.view(np.uint32)), f"T={T}: weights"
+        assert np.array_equal(ref.y.view(np.uint32), got.y.view(np.uint32)), f"T={T}: y differs"
+
+
 def test_topk_paths_agree(moe):
     """Below 2048 tokens the top-k runs one block per token, from 2048 one
     wave per token.  2047 and 2048 tokens give the same router tiling, so
