@@ -128,8 +128,19 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   __shared__ int32_t wcnt[16][kMaxExperts];
   __shared__ int32_t run[kMaxExperts];
   __shared__ int smem[40];
+  constexpr int PER = kSmallPairs / 1024;  // pairs per thread
   const int tid = threadIdx.x;
-  for (int p = tid; p < P; p += 1024) sid[p] = ids[p];
+  // The gating weights are requested with the ids, so the scatter at the
+  // end does not wait for a second round trip.
+  float wv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int p = tid + 1024 * j;
+    if (p < P) {
+      sid[p] = ids[p];
+      wv[j] = w_sorted ? topk_w[p] : 0.f;
+    }
+  }
   for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
   for (int e = tid; e < E; e += 1024) run[e] = 0;
   __syncthreads();
@@ -137,13 +148,16 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   const int count = tid < E ? run[tid] : 0;
   offsets_and_tiles(count, E, T, bm, with_shared, smem, offsets, run, tiles, ntiles, queue);
   __syncthreads();
-  for (int p = tid; p < P; p += 1024) {
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int p = tid + 1024 * j;
+    if (p >= P) continue;
     const int e = sid[p];
     if (e < 0 || e >= E) continue;
     const int i = run[e] + srank[p];
     sorted[i] = p;
     pos[p] = i;
-    if (w_sorted) w_sorted[i] = topk_w[p];
+    if (w_sorted) w_sorted[i] = wv[j];
   }
 }
 
