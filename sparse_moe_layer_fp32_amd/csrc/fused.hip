@@ -120,12 +120,31 @@ __device__ __forceinline__ uint32_t load_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One thread: wait until ctl[word] >= target, then acquire.  On running out,
-// record `flag` and return false.
-__device__ bool wait_count(uint32_t* ctl, int word, uint32_t target, uint32_t flag) {
-  for (uint32_t i = 0; load_relaxed(ctl + word) < target; ++i) {
+// The control code runs on all 64 lanes of one wave and keeps every value
+// that a loop or branch depends on uniform across the wave (lane 0 does the
+// atomics, readlane hands the result to the others).  A loop that only some
+// lanes of a wave run must not hold or precede a block barrier: the compiler
+// may then let the other lanes go on through the barrier without them (with
+// the tickets taken by thread 0 alone, it did: the rest of the block went on
+// to the hand-over barrier and re-read the previous ticket, forever).
+__device__ __forceinline__ uint32_t wave_load(const uint32_t* p) {
+  return __builtin_amdgcn_readfirstlane(load_relaxed(p));
+}
+
+__device__ __forceinline__ uint32_t wave_fetch_add(uint32_t* p, uint32_t v) {
+  uint32_t r = 0;
+  if ((threadIdx.x & 63) == 0)
+    r = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_amdgcn_readlane(r, 0);
+}
+
+// One whole wave: wait until ctl[word] >= target, then acquire.  On running
+// out, record `flag` and return false.
+__device__ bool wave_wait_count(uint32_t* ctl, int word, uint32_t target, uint32_t flag) {
+  for (uint32_t i = 0; wave_load(ctl + word) < target; ++i) {
     if (i == kSpinLimit) {
-      __hip_atomic_fetch_or(ctl + kCtlStatus, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_or(ctl + kCtlStatus, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -134,10 +153,14 @@ __device__ bool wait_count(uint32_t* ctl, int word, uint32_t target, uint32_t fl
   return true;
 }
 
-// The whole block waits; true when the count was reached.
+// The whole block waits (wave 0 polls); true when the count was reached.
 __device__ __forceinline__ bool block_wait(uint32_t* ctl, int word, uint32_t target, uint32_t flag,
                                            int* s_ok) {
-  if (threadIdx.x == 0) *s_ok = wait_count(ctl, word, target, flag) ? 1 : 0;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wid == 0) {
+    const bool ok = wave_wait_count(ctl, word, target, flag);
+    if (threadIdx.x == 0) *s_ok = ok ? 1 : 0;
+  }
   __syncthreads();
   return *s_ok != 0;
 }
@@ -253,28 +276,28 @@ __global__ __launch_bounds__(kFT) void fused_kernel(FusedArgs f) {
 
   int phase = 0, nr = -1;
   for (;;) {
-    // Next ticket (thread 0), handed to the block through LDS.
-    if (tid == 0) {
+    // Next ticket (wave 0), handed to the block through LDS.
+    if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
       int t = -1;
       while (phase < kNumPhases) {
         if ((phase == kPhGu || phase == kPhDown) && nr < 0) {
           // Without the permutation there are no routed tiles to run.
-          nr = wait_count(ctl, kCtlPermDone, 1, kStPerm)
-                   ? min(static_cast<int>(load_relaxed(ctl + kCtlNtiles)), f.tile_cap)
+          nr = wave_wait_count(ctl, kCtlPermDone, 1, kStPerm)
+                   ? min(static_cast<int>(wave_load(ctl + kCtlNtiles)), f.tile_cap)
                    : 0;
         }
         const int units = phase_units(s, phase, nr);
         if (units > 0) {
-          t = static_cast<int>(__hip_atomic_fetch_add(ctl + kCtlTicket + phase, 1u,
-                                                      __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT));
+          t = static_cast<int>(wave_fetch_add(ctl + kCtlTicket + phase, 1u));
           if (t < units) break;
         }
         ++phase;
       }
-      s_ctl[0] = phase;
-      s_ctl[1] = t;
-      s_ctl[2] = nr;
+      if (tid == 0) {
+        s_ctl[0] = phase;
+        s_ctl[1] = t;
+        s_ctl[2] = nr;
+      }
     }
     __syncthreads();
     phase = s_ctl[0];

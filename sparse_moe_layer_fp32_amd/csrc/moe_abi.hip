@@ -296,7 +296,6 @@ moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* rou
 }
 
 // ---- single launch (small batches): the same steps in one persistent grid.
-constexpr bool kFusedLaunchDisabled = true;
 
 moe_status forward_fused_impl(const moe_config* c, const uint16_t* x, const float* router_w,
                               const float* router_bias, const uint16_t* w_gate,
@@ -322,13 +321,6 @@ moe_status forward_fused_impl(const moe_config* c, const uint16_t* x, const floa
   Plan p;
   make_plan(c, &p);
   if ((st = check_ws(p, ws, ws_bytes))) return st;
-  // Switched off: on its first run on an MI355X the single-launch kernel did
-  // not finish (smallest layer shape, 512 blocks); no mistake that explains
-  // it has been found, so nothing is launched until one is.
-  if (kFusedLaunchDisabled)
-    return fail(MOE_ERR_UNSUPPORTED,
-                "single-launch forward is switched off: its kernel did not finish on gfx950 and "
-                "the cause is not yet known; use moe_forward");
   if (p.T == 0) return ok();
 
   moe::FusedArgs f{};

@@ -168,9 +168,6 @@ def test_fused_errors_before_launch():
         big = moe.make_config(T, 4096, 288, k, 1280, 1280)
         st = lib.moe_forward_fused(ctypes.byref(big), *args, moe.moe_workspace_size(big), None)
         assert st == moe.MOE_ERR_UNSUPPORTED and "single-launch" in moe.moe_last_error()
-    # switched off: a valid call is refused before anything is launched
-    st = lib.moe_forward_fused(ctypes.byref(cfg), *args, need, None)
-    assert st == moe.MOE_ERR_UNSUPPORTED and "switched off" in moe.moe_last_error()
     total = moe.moe_workspace_size(cfg)
     c_off, c_nb = moe.moe_workspace_view(cfg, moe.MOE_WS_FUSED_CTL)
     s_off, s_nb = moe.moe_workspace_view(cfg, moe.MOE_WS_FUSED_STATUS)

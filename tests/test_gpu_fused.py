@@ -16,13 +16,7 @@ import oracle
 import synth
 from tests import gpu_util as gu
 
-pytestmark = [
-    pytest.mark.gpu,
-    pytest.mark.skip(reason="moe_forward_fused is switched off: its kernel did not finish on "
-                            "its first MI355X run (smallest case, 180 s) and the cause is not "
-                            "yet known; the entry point returns MOE_ERR_UNSUPPORTED"),
-]
-
+pytestmark = pytest.mark.gpu
 
 @pytest.fixture(autouse=True)
 def _name_case(request):
