@@ -26,8 +26,9 @@
 // grid always drains.
 //
 // Every unit computes exactly what the multi-launch path computes (same
-// router tiles and k splits, same top-k keys and sums, same 64 x 128 GEMM
-// tiles, same combine order), so the two give bit-identical outputs.
+// router tiles and k splits, same top-k keys and sums, the same k order for
+// every GEMM output, same combine order), so the two give bit-identical
+// outputs.
 //
 // Memory ordering: a finished unit waits for its own stores, meets the
 // block barrier, and one thread raises the counter with an agent-scope
@@ -44,11 +45,19 @@ namespace moe {
 namespace {
 
 constexpr int kFT = 256;  // threads per block (4 waves)
-using GemmCfg = Cfg<64, 128, 64, 2, 2, 3>;
-constexpr int kGemmLds = GemmCfg::LDS_BYTES;
+// GEMM tiles of 64 rows, one block per CU, each keeping 80-120 KB of weights
+// in flight: gate/up 128 weight rows at k step 128 with a 3-deep ring (H is
+// a multiple of 128); down 256 output columns (the four waves side by side)
+// at k step 64 with a 3-deep ring when H is a multiple of 256, else 128
+// columns with a 6-deep ring (I is a multiple of 64).
+using GuCfg = Cfg<64, 128, 128, 2, 2, 3>;
+using DnCfg = Cfg<64, 128, 64, 2, 2, 6>;
+using DnWideCfg = Cfg<64, 256, 64, 1, 4, 3>;
+constexpr int kDnLds = DnCfg::LDS_BYTES > DnWideCfg::LDS_BYTES ? DnCfg::LDS_BYTES : DnWideCfg::LDS_BYTES;
+constexpr int kGemmLds = GuCfg::LDS_BYTES > kDnLds ? GuCfg::LDS_BYTES : kDnLds;
 constexpr int kPermLds = (2 * kFusedMaxPairs + 4 * kMaxExperts + kMaxExperts + 16) * 4;
 constexpr int kTopkLds = 4 * kMaxExperts * (4 + 8);  // per wave: logits and keys
-static_assert(kTopkLds <= Cfg<64, 128, 64, 2, 2, 3>::LDS_BYTES, "top-k LDS");
+static_assert(kTopkLds <= kGemmLds, "top-k LDS");
 constexpr int kFusedLds = kGemmLds > kRouterTileLds ? (kGemmLds > kPermLds ? kGemmLds : kPermLds)
                                                     : (kRouterTileLds > kPermLds ? kRouterTileLds
                                                                                  : kPermLds);
@@ -76,6 +85,7 @@ struct Shape {
   int ntg_s;     // shared gate/up column tiles per row tile
   int ntg;       // routed gate/up column tiles per row tile
   int ntd;       // down column tiles per row tile
+  int dn_wide;   // down tiles of 256 columns (else 128)
   int n_topk, n_comb;
 };
 
@@ -90,7 +100,8 @@ __device__ __forceinline__ Shape shape_of(const FusedArgs& f) {
   s.ns = f.g.Is > 0 ? nmt : 0;
   s.ntg_s = f.g.Is / 64;
   s.ntg = f.g.I / 64;
-  s.ntd = f.g.H / 128;
+  s.dn_wide = f.g.H % 256 == 0;
+  s.ntd = f.g.H / (s.dn_wide ? 256 : 128);
   s.n_topk = (s.T + 3) / 4;
   s.n_comb = static_cast<int>((static_cast<int64_t>(s.T) * (f.g.H / 8) + kFT - 1) / kFT);
   return s;
@@ -266,9 +277,22 @@ __device__ int fused_permute(const FusedArgs& f, const Shape& s, uint8_t* smem) 
   return min(ttot, f.tile_cap);
 }
 
+// A down tile (direct stores: the waves go on to other units).
+__device__ __forceinline__ void down_tile(const ExpertArgs& g, uint8_t* smem, TileCoord tc, int e,
+                                          int row0, int wide) {
+  if (wide)
+    gemm_tile<1, 64, 256, 64, 1, 4, 3, 0, 0, false>(g, smem, tc, e, row0);
+  else
+    gemm_tile<1, 64, 128, 64, 2, 2, 6, 0, 0, false>(g, smem, tc, e, row0);
+}
+
 __global__ __launch_bounds__(kFT) void fused_kernel(FusedArgs f) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kFusedLds];
-  __shared__ int s_ctl[4];
+  // One LDS array for everything, the hand-over words in its last 16 bytes:
+  // with a second __shared__ variable the compiler makes every LDS read that
+  // follows a weight DMA wait for all DMAs in flight (vmcnt(0)), which drains
+  // the GEMM rings at every k substep (the GEMM units ran 2-3x slower).
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kFusedLds + 16];
+  int* const s_ctl = reinterpret_cast<int*>(smem + kFusedLds);
   const int tid = threadIdx.x;
   uint32_t* ctl = f.ctl;
   const Shape s = shape_of(f);
@@ -315,7 +339,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(FusedArgs f) {
       }
       case kPhSharedGu: {
         const int j = t / s.ntg_s;
-        gemm_tile<0, 64, 128, 64, 2, 2, 3, 0>(f.g, smem, TileCoord{0, t % s.ntg_s}, E, 64 * j);
+        gemm_tile<0, 64, 128, 128, 2, 2, 3, 0>(f.g, smem, TileCoord{0, t % s.ntg_s}, E, 64 * j);
         block_signal(ctl, kCtlSharedGu + j);
         break;
       }
@@ -341,7 +365,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(FusedArgs f) {
       case kPhSharedDown: {
         const int j = t / s.ntd;
         if (block_wait(ctl, kCtlSharedGu + j, s.ntg_s, kStSharedGu, &s_ctl[3]))
-          gemm_tile<1, 64, 128, 64, 2, 2, 3, 0, 0, false>(f.g, smem, TileCoord{0, t % s.ntd}, E, 64 * j);
+          down_tile(f.g, smem, TileCoord{0, t % s.ntd}, E, 64 * j, s.dn_wide);
         block_signal(ctl, kCtlDownDone);
         break;
       }
@@ -349,7 +373,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(FusedArgs f) {
         const int i = t / s.ntg;
         const int2 tile = f.tiles[i];
         if (tile_ok(tile, E, s.P))
-          gemm_tile<0, 64, 128, 64, 2, 2, 3, 0>(f.g, smem, TileCoord{0, t % s.ntg}, tile.x,
+          gemm_tile<0, 64, 128, 128, 2, 2, 3, 0>(f.g, smem, TileCoord{0, t % s.ntg}, tile.x,
                                                 tile.y);
         block_signal(ctl, kCtlTileGu + i);
         break;
@@ -359,8 +383,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(FusedArgs f) {
         if (block_wait(ctl, kCtlTileGu + i, s.ntg, kStGu, &s_ctl[3])) {
           const int2 tile = f.tiles[i];
           if (tile_ok(tile, E, s.P))
-            gemm_tile<1, 64, 128, 64, 2, 2, 3, 0, 0, false>(f.g, smem, TileCoord{0, t % s.ntd}, tile.x,
-                                                  tile.y);
+            down_tile(f.g, smem, TileCoord{0, t % s.ntd}, tile.x, tile.y, s.dn_wide);
         }
         block_signal(ctl, kCtlDownDone);
         break;
@@ -389,7 +412,7 @@ int fused_grid() {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  return 2 * cus;  // two blocks per CU (LDS and registers allow two)
+  return cus;  // one block per CU (the GEMM rings take most of the LDS)
 }
 
 }  // namespace
