@@ -288,6 +288,44 @@ def measure(wl, moe, synth, experts_host, copies, steps, warmup):
     return out, ids_h
 
 
+def measure_single_launch(wl, moe, synth, copies, steps, warmup, ms_multi):
+    """moe_forward_fused (the whole layer in one launch) on the same inputs and
+    weight copies as the multi-launch measurement; its output is checked equal,
+    bit for bit, to moe_forward's on the first copy."""
+    import numpy as np
+    import torch
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    x = dev(synth.gen_x(wl))
+    rw_h, rb_h, _ = synth.gen_router(wl)
+    rw, rb = dev(rw_h), (dev(rb_h) if wl.use_bias else None)
+    cfg = moe.make_config(wl.T, wl.H, wl.E, wl.k, wl.I, wl.Is, wl.routed_scaling,
+                          wl.renormalize, wl.limit, wl.limit_shared)
+    ws = moe.alloc_workspace(cfg)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    y_ref = torch.empty_like(y)
+    moe.moe_forward(cfg, x, rw, rb, *copies[0], y_ref, None, None, ws)
+    moe.moe_forward_fused(cfg, x, rw, rb, *copies[0], y, None, None, ws)
+    torch.cuda.synchronize()
+    identical = bool(torch.equal(y.view(torch.int16), y_ref.view(torch.int16)))
+    for i in range(warmup):
+        moe.moe_forward_fused(cfg, x, rw, rb, *copies[i % len(copies)], y, None, None, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_forward_fused(cfg, x, rw, rb, *copies[i % len(copies)], y, None, None, ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del ws
+    return dict(ms_per_step=round(ms, 5), tokens_per_s=round(wl.T / (ms * 1e-3), 1),
+                vs_multi_launch=round(ms_multi / ms, 3), identical_to_multi_launch=identical)
+
+
 def measure_fp8(wl, moe, synth, copies8, shared, steps, warmup):
     """moe_forward_fp8 (routed experts as e4m3 codes + row scales) on the
     workload's inputs, the copies of the FP8 weights rotated per step."""
@@ -466,6 +504,11 @@ def main():
         # Second workloads on the same kernels: the predecessor Step-3's MoE shape and the
         # dense SwiGLU FFN of the first layers.
         rec["workloads"] = {}
+        # The same decode step in one launch (moe_forward_fused)
+        rec["workloads"]["decode_single_launch"] = measure_single_launch(
+            wl, moe, synth, copies, args.steps, args.warmup, res["ms_per_step"])
+        log(f"[bench] decode single launch: "
+            f"{rec['workloads']['decode_single_launch']['ms_per_step']:.4f} ms/step")
         sw = synth.WORKLOADS["step3"]
         log(f"[bench] step3 T={sw.T} (H {sw.H}, E {sw.E}, k {sw.k}, I {sw.I})")
         s_host = synth.gen_experts(sw)

@@ -201,7 +201,10 @@ int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape) {
 // ring, one block per CU; gate/up 64 h columns (128 weight rows) with k step
 // 128, so every weight row is read in 256-byte pieces; down 256 output
 // columns, k step 64, 8 waves (128 columns and 4 waves when H is not a
-// multiple of 256).  The e4m3 kernels keep 64 x 128 tiles with k step 64.
+// multiple of 256).  The e4m3 kernels: 64 x 256 tiles, k step 64, 4-deep
+// ring, 8 waves (their k steps carry half the bytes of a bf16 step; the
+// shared expert's bf16 tiles in them take the whole 160 KB of LDS), else
+// 64 x 128 with a 3-deep ring.
 hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream,
                          int fp8) {
   const int maxn = std::max(a.I, a.Is);
@@ -209,6 +212,8 @@ hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipS
     if (shape == kTileBig)
       return launch_persistent<0, 256, 256, 64, 2, 4, 3, 1, 1>(a, (maxn + 127) / 128, a.queue,
                                                                stream);
+    if (a.I % 128 == 0 && a.Is % 128 == 0)
+      return launch_one<0, 64, 256, 64, 2, 4, 4, 1>(a, tile_capacity, maxn / 128, stream);
     return launch_one<0, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, (maxn + 63) / 64, stream);
   }
   if (shape == kTileBig)
@@ -223,6 +228,8 @@ hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStr
     if (shape == kTileBig)
       return launch_persistent<1, 256, 256, 64, 2, 4, 3, 1, 1>(a, a.H / 256, a.queue + kNumXcd,
                                                                stream);
+    if (a.H % 256 == 0)
+      return launch_one<1, 64, 256, 64, 2, 4, 4, 1>(a, tile_capacity, a.H / 256, stream);
     return launch_one<1, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, a.H / 128, stream);
   }
   if (shape == kTileBig)

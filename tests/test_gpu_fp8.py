@@ -66,6 +66,8 @@ CASES = {
     "ragged": dict(T=333, H=512, E=24, k=6, I=192, Is=128, hot_experts=4, bias_var=0.1),
     "no_shared": dict(T=77, H=256, E=16, k=4, I=64, Is=0, bias_var=0.5),
     "clamped": dict(T=96, H=256, E=16, k=4, I=128, Is=64, limit=0.05, limit_shared=0.1),
+    # small tiles 256 wide (I and Is multiples of 128, H of 256), ragged expert rows
+    "wide_small": dict(T=150, H=512, E=12, k=4, I=256, Is=128, bias_var=0.3),
     # 256 x 256 tiles
     "big_tile": dict(T=1100, H=512, E=8, k=4, I=256, Is=128, bias_var=0.5),
     "big_tile_no_shared": dict(T=1500, H=768, E=6, k=3, I=384, Is=0, bias_var=0.2),
