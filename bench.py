@@ -117,7 +117,7 @@ def summarize_profiles(d):
         path = os.path.join(d, f"kt_{wl}", "run_kernel_stats.csv")
         rows = list(csv.DictReader(open(path)))
         lines = [f"# Kernel durations, {wl} workload (rocprofv3 kernel trace)", "",
-                 "Command (from /tmp with TMPDIR=/tmp; DIR = gpurun_out of the repo):", "",
+                 "Command (from /tmp with TMPDIR=/tmp; DIR = an output directory):", "",
                  "```", PROFILE_COMMANDS[f"kt_{wl}"], "```", "",
                  "| Kernel | Calls | Average us | Min us | Max us | Share |",
                  "|---|---|---|---|---|---|"]
