@@ -178,18 +178,14 @@ moe_status moe_forward_fp8(const moe_config* cfg, const uint16_t* x, const float
 
 /* The same layer forward as moe_forward in ONE kernel launch, for small
  * batches (decoding): tokens <= 256 and tokens * top_k <= 2048, else
- * MOE_ERR_UNSUPPORTED.
- *
- * CURRENTLY SWITCHED OFF: after validating its arguments every call returns
- * MOE_ERR_UNSUPPORTED and launches nothing.  The kernel did not finish on
- * its first run on an MI355X and the cause is not yet known; moe_forward
- * computes the same results.  The contract below is the one the kernel
- * implements. */
+ * MOE_ERR_UNSUPPORTED (checked before anything is enqueued).  On an MI355X
+ * it is slower than moe_forward at every measured batch size; it serves
+ * callers that want a single launch per layer. */
 /* It is the fused expert backend that the sglang-jax issue "[Feature] Support Step 3.5 Flash (StepFun) Model" names as the
  * performance switch after the grouped-matmul path ("Reuse map",
  * "Implementation strategy").  Arguments, layouts and outputs are those of
- * moe_forward, and so are the results, bit for bit: the launch runs the
- * same tiles in the same arithmetic order.
+ * moe_forward, and so are the results, bit for bit: every output is formed
+ * in the same arithmetic order.
  *
  * Workspace: moe_workspace_size(cfg) bytes, as for moe_forward.  Its
  * control words (MOE_WS_FUSED_CTL below, under 5 KB) must be zero before
