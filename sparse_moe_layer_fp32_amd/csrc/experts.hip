@@ -197,11 +197,12 @@ int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape) {
 // covered by the other's MFMAs), split ring with A 2-deep and B 3-deep, the
 // whole 160 KB of LDS (e4m3 launches too: their B stages are half the size,
 // and the shared expert's bf16 tiles in them take the same ring).
-// Small (few rows per expert, the GEMMs stream weights): 64 rows, 3-deep
-// ring, one block per CU; gate/up 64 h columns (128 weight rows) with k step
-// 128, so every weight row is read in 256-byte pieces; down 256 output
-// columns, k step 64, 8 waves (128 columns and 4 waves when H is not a
-// multiple of 256).  The e4m3 kernels: 64 x 256 tiles, k step 64, 4-deep
+// Small (few rows per expert, the GEMMs stream weights): 64 rows, one block
+// per CU; gate/up 128 h columns (256 weight rows), k step 64, 8 waves, 4-deep
+// ring when I and Is are multiples of 128 (else 64 h columns, k step 128, 4
+// waves, 3-deep: every weight row read in 256-byte pieces); down 256 output
+// columns, k step 64, 8 waves, 3-deep (128 columns and 4 waves when H is not
+// a multiple of 256).  The e4m3 kernels: 64 x 256 tiles, k step 64, 4-deep
 // ring, 8 waves (their k steps carry half the bytes of a bf16 step; the
 // shared expert's bf16 tiles in them take the whole 160 KB of LDS), else
 // 64 x 128 with a 3-deep ring.
@@ -219,6 +220,8 @@ hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipS
   if (shape == kTileBig)
     return launch_persistent<0, 256, 256, 64, 2, 4, 3, 0, 1>(a, (maxn + 127) / 128, a.queue,
                                                              stream);
+  if (a.I % 128 == 0 && a.Is % 128 == 0)
+    return launch_one<0, 64, 256, 64, 2, 4, 4>(a, tile_capacity, maxn / 128, stream);
   return launch_one<0, 64, 128, 128, 2, 2, 3>(a, tile_capacity, (maxn + 63) / 64, stream);
 }
 

@@ -84,6 +84,8 @@ SMALL = {
     "zero_scaling": dict(T=40, H=256, E=16, k=4, I=64, Is=64, routed_scaling=0.0),
     "full_router": dict(T=40, H=4096, E=288, k=8, I=64, Is=64),
     "wide_inter": dict(T=130, H=384, E=10, k=3, I=320, Is=192, bias_var=0.3),
+    # small tiles 256 weight rows wide (I and Is multiples of 128), ragged expert rows
+    "wide_small": dict(T=150, H=512, E=12, k=4, I=256, Is=128, bias_var=0.3),
     # enough rows per expert for the 256 x 256 tile shape, ragged last tiles
     "big_tile": dict(T=1100, H=512, E=8, k=4, I=256, Is=128, bias_var=0.5),
     "big_tile_no_shared": dict(T=1500, H=768, E=6, k=3, I=384, Is=0, bias_var=0.2),
