@@ -70,7 +70,7 @@ def _load():
                                        vp, vp, ctypes.c_int]
         lib.oracle_expert.argtypes = [i32, i32, dbl, vp, i64, vp, vp, vp, vp, vp, ctypes.c_int]
         lib.oracle_forward_fp8.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                           i64, vp, vp, vp, ctypes.c_int]
+                                           i64, vp, vp, vp, vp, ctypes.c_int]
         lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
         lib.oracle_permute.argtypes = [i64, i32, i32, vp, vp, vp, vp]
         lib.oracle_hardware_threads.argtypes = []
@@ -83,7 +83,13 @@ def hardware_threads() -> int:
 
 
 def default_threads() -> int:
-    return max(1, min(16, hardware_threads()))
+    """Threads for the oracle: the CPUs this process may run on, at most 16
+    (the host CPU share that goes with one GPU on the machines this runs
+    on); MOE_ORACLE_THREADS overrides."""
+    env = os.environ.get("MOE_ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    return max(1, min(16, hardware_threads(), len(os.sched_getaffinity(0))))
 
 
 def make_cfg(T, H, E, k, I, Is, routed_scaling=3.0, renormalize=True, limit=0.0,
@@ -152,13 +158,14 @@ def forward(cfg: Cfg, inp, tokens=None, forced_ids=None, threads=None):
     return dict(y=y, ids=ids, w=w)
 
 
-def forward_fp8(cfg: Cfg, inp, fp8, tokens=None, threads=None):
+def forward_fp8(cfg: Cfg, inp, fp8, tokens=None, forced_ids=None, threads=None):
     """forward with the routed experts' weights from `fp8` (synth.Fp8Experts:
     e4m3 codes and per-row scales); the shared expert from `inp`.
     -> dict(y [n,H] f64, ids, w)."""
     x = _c(inp.x, np.uint16)
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
     n = cfg.T if tok is None else tok.size
+    fid = None if forced_ids is None else _c(np.asarray(forced_ids, np.int32), np.int32)
     y = np.empty((n, cfg.H), np.float64)
     ids = np.empty((n, cfg.k), np.int32)
     w = np.empty((n, cfg.k), np.float64)
@@ -167,7 +174,7 @@ def forward_fp8(cfg: Cfg, inp, fp8, tokens=None, threads=None):
             _c(fp8.s_gate, np.float32), _c(fp8.s_up, np.float32), _c(fp8.s_down, np.float32),
             _c(inp.ws_gate, np.uint16), _c(inp.ws_up, np.uint16), _c(inp.ws_down, np.uint16)]
     rc = _load().oracle_forward_fp8(ctypes.byref(cfg), _p(x), *[_p(a) for a in args], _p(tok), n,
-                                    _p(y), _p(ids), _p(w), threads or default_threads())
+                                    _p(fid), _p(y), _p(ids), _p(w), threads or default_threads())
     if rc:
         raise ValueError(f"oracle_forward_fp8 failed ({rc})")
     return dict(y=y, ids=ids, w=w)

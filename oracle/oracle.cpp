@@ -77,9 +77,10 @@ double swiglu(double g, double u, double limit) {
 // OCP FP8 E4M3 ("e4m3fn") code -> value, from the format's definition:
 // bit 7 sign, bits 6..3 exponent with bias 7, bits 2..0 mantissa; exponent 0
 // holds the subnormals (mantissa/8) * 2^-6; all-ones exponent and mantissa
-// is NaN (no infinities).  The FP8 checkpoints of the model card ("Official
-// weights: BF16 (also FP8 ...)" in the sglang-jax issue's model configuration)
-// store weights this way with a scale per output row.
+// is NaN (no infinities).  The sglang-jax issue's "Model configuration" lists
+// FP8 among the official weight formats and says nothing more about it; the
+// OCP E4M3 codes with one fp32 scale per output row are this oracle's
+// reading of that format (not a fact the pages state).
 double e4m3_to_double(uint8_t c) {
   const int sign = c >> 7, ex = (c >> 3) & 15, man = c & 7;
   double v;
@@ -99,12 +100,26 @@ struct Bf16W {
   int64_t cols;
   double operator()(int64_t r, int64_t c) const { return bf16_to_double(p[r * cols + c]); }
 };
+// The 256 values of the e4m3 codes, each from e4m3_to_double (filled once;
+// a weight read looks its code up instead of decoding it again).
+struct E4m3Values {
+  double v[256];
+  E4m3Values() {
+    for (int c = 0; c < 256; ++c) v[c] = e4m3_to_double(static_cast<uint8_t>(c));
+  }
+};
+const E4m3Values& e4m3_values() {
+  static const E4m3Values table;
+  return table;
+}
+
 struct Fp8W {
   const uint8_t* p;
   const float* scale;
   int64_t cols;
+  const double* value = e4m3_values().v;
   double operator()(int64_t r, int64_t c) const {
-    return e4m3_to_double(p[r * cols + c]) * static_cast<double>(scale[r]);
+    return value[p[r * cols + c]] * static_cast<double>(scale[r]);
   }
 };
 
@@ -263,7 +278,8 @@ int oracle_forward(const Cfg* c, const uint16_t* x, const float* wg, const float
   return 0;
 }
 
-// oracle_forward with the routed experts' weights in FP8: e4m3 codes
+// oracle_forward with the routed experts' weights in FP8 (forced_ids as
+// there): e4m3 codes
 // w8_gate/w8_up [E][I][H], w8_down [E][H][I] and fp32 scales per output row
 // s_gate/s_up [E][I], s_down [E][H]; weight = e4m3_to_double(code) * scale.
 // The shared expert stays bf16.
@@ -271,8 +287,8 @@ int oracle_forward_fp8(const Cfg* c, const uint16_t* x, const float* wg, const f
                        const uint8_t* w8_gate, const uint8_t* w8_up, const uint8_t* w8_down,
                        const float* s_gate, const float* s_up, const float* s_down,
                        const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
-                       const int64_t* tokens, int64_t ntok, double* y, int32_t* ids_out,
-                       double* w_out, int threads) {
+                       const int64_t* tokens, int64_t ntok, const int32_t* forced_ids, double* y,
+                       int32_t* ids_out, double* w_out, int threads) {
   if (!cfg_ok(c) || !x || !wg || !w8_gate || !w8_up || !w8_down || !s_gate || !s_up || !s_down ||
       !y || ntok < 0)
     return 1;
@@ -284,7 +300,10 @@ int oracle_forward_fp8(const Cfg* c, const uint16_t* x, const float* wg, const f
     std::vector<int32_t> ids(c->k);
     for (int h = 0; h < c->H; ++h) xr[h] = bf16_to_double(x[t * c->H + h]);
     router_row(*c, xr.data(), wg, bias, s.data(), key.data());
-    select_topk(*c, key.data(), ids.data());
+    if (forced_ids)
+      std::copy(forced_ids + n * c->k, forced_ids + (n + 1) * c->k, ids.begin());
+    else
+      select_topk(*c, key.data(), ids.data());
     gating_weights(*c, s.data(), ids.data(), w.data());
     for (int j = 0; j < c->k; ++j) {
       const int64_t e = ids[j];
