@@ -24,3 +24,21 @@ def full_experts():
     host = synth.gen_experts(wl)
     dev = tuple(gu.to_dev(a) for a in host)
     return host, dev
+
+
+@pytest.hookimpl(trylast=True)
+def pytest_runtest_logfinish(nodeid, location):
+    """Flush the progress line after every test, so that a long GPU session
+    shows each test's end as it happens (stdout to a file or pipe is block
+    buffered)."""
+    tr = _CONFIG[0].pluginmanager.get_plugin("terminalreporter") if _CONFIG else None
+    if tr is not None:
+        tr._tw.flush()
+
+
+_CONFIG = []
+
+
+@pytest.hookimpl(tryfirst=True)
+def pytest_sessionstart(session):
+    _CONFIG.append(session.config)

@@ -168,7 +168,7 @@ def test_fused_over_limit_enqueues_nothing(moe):
 def test_fused_full_shape(moe, full_experts, T):
     """Decoding batches at the full layer shape (4096 -> 1280 -> 4096, 288
     experts, top 8, shared expert): bit-identical to the multi-launch path,
-    and the oracle on sampled tokens."""
+    and the oracle on every token."""
     wl = synth.WORKLOADS["decode"]
     host, dev = full_experts
     inp = synth.make_inputs(wl, experts=host)
@@ -181,7 +181,31 @@ def test_fused_full_shape(moe, full_experts, T):
     x_T = inp.x[:T]
     ref = oracle.route(oracle.cfg_of(wlT), x_T, inp.router_w, inp.router_b, want_keys=True)
     rep = gu.compare_route(wlT, b["ids"], b["w"], ref)
-    toks = np.array(sorted(set(range(min(T, 6))) | {T - 1}), np.int64)
+    toks = np.arange(T, dtype=np.int64)
     y_ref = gu.oracle_y_for(wl, inp, toks, b["ids"], rep.mismatched)
     err, M = gu.check_y(b["y"][toks], y_ref, f"decode T={T}")
     gu.note(f"  decode T={T}: identical to multi-launch; oracle max err {err:.3e} M {M:.3e}")
+
+
+@pytest.mark.parametrize("levels", [False, True])
+def test_fused_ties(moe, levels):
+    """Router weight 0: all scores 1/2; without a bias every key ties (ids
+    0..k-1), with a bias of five exact levels the keys tie within each level
+    (the lowest-numbered experts of the top level).  The single launch's own
+    top-k body must rank equal keys lower index first, as moe_forward does."""
+    wl = synth.WORKLOADS["tiny"].with_(name="fused_ties", T=64, H=512, E=300, k=8, I=64, Is=64)
+    inp = synth.make_inputs(wl)
+    inp.router_w[:] = 0.0
+    if levels:
+        rng = np.random.default_rng(5)
+        inp.router_b = rng.choice(np.array([-0.5, -0.25, 0.0, 0.25, 0.5], np.float32), wl.E)
+        want = np.nonzero(inp.router_b == np.float32(0.5))[0][: wl.k]
+    else:
+        inp.router_b = np.zeros(wl.E, np.float32)
+        want = np.arange(wl.k)
+    d = gu.upload(inp)
+    a = _run(moe, wl, d, False)
+    b = _run(moe, wl, d, True)
+    _assert_identical(a, b, "ties")
+    _check_ctl_clear(moe, b)
+    assert np.all(b["ids"] == want) and np.all(b["w"] == np.float32(0.375))
