@@ -157,11 +157,13 @@ moe_status moe_forward_timed(const moe_config* cfg, const uint16_t* x, const flo
                              float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream,
                              hipEvent_t* events, int n_events);
 
-/* moe_forward with the routed experts' weights in FP8: the model card lists
- * FP8 among the official weight formats (sglang-jax issue, "Model
- * configuration": "Official weights: BF16 (also FP8 / ...)").  Each routed
- * weight is decode(code) * scale of its output row, code an OCP FP8 E4M3
- * ("e4m3fn": bias 7, no infinities, max 448) byte:
+/* moe_forward with the routed experts' weights in FP8.  The sglang-jax issue
+ * "[Feature] Support Step 3.5 Flash (StepFun) Model", section "Model
+ * configuration", lists FP8 among the model's official weight formats beside
+ * BF16 and says nothing more about it; the layout below (OCP E4M3 codes with
+ * one fp32 scale per output row) is this library's reading of that format.
+ * Each routed weight is decode(code) * scale of its output row, code an OCP
+ * FP8 E4M3 ("e4m3fn": bias 7, no infinities, max 448) byte:
  *   w8_gate, w8_up  [E][I][H] uint8 codes;  scale_gate, scale_up  [E][I] fp32
  *   w8_down         [E][H][I] uint8 codes;  scale_down            [E][H] fp32
  * The shared expert stays bf16 (ws_gate/ws_up/ws_down as in moe_forward).
@@ -178,14 +180,13 @@ moe_status moe_forward_fp8(const moe_config* cfg, const uint16_t* x, const float
 
 /* The same layer forward as moe_forward in ONE kernel launch, for small
  * batches (decoding): tokens <= 256 and tokens * top_k <= 2048, else
- * MOE_ERR_UNSUPPORTED (checked before anything is enqueued).  On an MI355X
- * it is slower than moe_forward at every measured batch size; it serves
- * callers that want a single launch per layer. */
-/* It is the fused expert backend that the sglang-jax issue "[Feature] Support Step 3.5 Flash (StepFun) Model" names as the
- * performance switch after the grouped-matmul path ("Reuse map",
- * "Implementation strategy").  Arguments, layouts and outputs are those of
- * moe_forward, and so are the results, bit for bit: every output is formed
- * in the same arithmetic order.
+ * MOE_ERR_UNSUPPORTED (checked before anything is enqueued).  It is the
+ * fused expert backend that the sglang-jax issue names as the performance
+ * switch to follow the grouped-matmul path ("Reuse map", "Implementation
+ * strategy").  On an MI355X it is slower than moe_forward at every measured
+ * batch size; it serves callers that want a single launch per layer.
+ * Arguments, layouts and outputs are those of moe_forward, and so are the
+ * results, bit for bit: every output is formed in the same arithmetic order.
  *
  * Workspace: moe_workspace_size(cfg) bytes, as for moe_forward.  Its
  * control words (MOE_WS_FUSED_CTL below, under 5 KB) must be zero before

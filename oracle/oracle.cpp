@@ -9,16 +9,17 @@
 //
 //  * sglang-jax issue "[Feature] Support Step 3.5 Flash (StepFun) Model",
 //    section "Model configuration", MoE bullet: 288 routed experts plus one
-//    shared expert of intermediate 1280, top-8, sigmoid routing computed in
-//    fp32, router bias, normalised top-k weights, routed scaling 3.0; and the
-//    clamped-SwiGLU bullet (a limit of 0.0 means no clamp).
+//    shared expert of intermediate 1280, top-8, a sigmoid router evaluated
+//    in fp32, a router bias, top-k weights normalised and scaled by 3.0; and
+//    the clamped-SwiGLU bullet (a limit of zero disables the clamp).
 //  * same issue, "Key difficulties", item 1: the sigmoid scores are taken in
 //    fp32; the router bias only decides which experts are selected; the
-//    gating weights are gathered from the bias-free sigmoid scores, then
+//    gating weights come from the scores without the bias, then are
 //    normalised over the selected experts and multiplied by the routed
 //    scaling factor 3.0.
-//  * same issue, "Reuse map": experts are SwiGLU MLPs ("SiLU-and-mul"), the
-//    clamp is an elementwise branch of that activation.
+//  * same issue, "Reuse map": experts are SwiGLU MLPs (SiLU of the gate
+//    times the up projection), with the clamp as an elementwise option of
+//    that activation.
 //  * llm-atlas Step-3.5-Flash model card, "Raw config fields": hidden_size,
 //    moe_num_experts, moe_top_k, moe_intermediate_size, share_expert_dim,
 //    norm_expert_weight, moe_router_activation (sigmoid),
@@ -331,7 +332,7 @@ int oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
   return 0;
 }
 
-// One SwiGLU expert applied row by row (the "per-expert loop"):
+// One SwiGLU expert applied row by row (the per-expert loop):
 // rows [n][H] bf16 -> h [n][I] (the activation SiLU(g)*u) and o [n][H].
 int oracle_expert(int32_t H, int32_t I, double limit, const uint16_t* rows, int64_t n,
                   const uint16_t* gate, const uint16_t* up, const uint16_t* down, double* h,

@@ -2,7 +2,7 @@
 //
 // Each routed expert is a SwiGLU MLP H -> I -> H (sglang-jax issue
 // "[Feature] Support Step 3.5 Flash (StepFun) Model", "Model configuration"
-// and "Reuse map": SiLU-and-mul with an elementwise clamp branch; llm-atlas
+// and "Reuse map": SiLU of the gate times up, optionally clamped; llm-atlas
 // Step-3.5-Flash card, raw fields moe_intermediate_size 1280 and
 // share_expert_dim 1280).  The pairs were sorted by expert, so expert e owns
 // rows [offsets[e], offsets[e+1]) of the sorted order; the shared expert is
