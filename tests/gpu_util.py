@@ -163,8 +163,10 @@ def compare_route(wl, gpu_ids, gpu_w, ref) -> RouteReport:
         assert np.all(gpu_ids[:, :-1][tied] < gpu_ids[:, 1:][tied]), \
             "exactly equal keys not listed lower index first"
     swaps = int(np.count_nonzero(np.any(gpu_ids != oids, 1) & same))
-    ties = int(np.count_nonzero(gap == 0)) + (
-        int(np.count_nonzero(np.any(ko[:, :-1] == ko[:, 1:], 1))) if k > 1 else 0)
+    tied = gap == 0  # an exact tie at the cut, or between two selected experts
+    if k > 1:
+        tied |= np.any(ko[:, :-1] == ko[:, 1:], 1)
+    ties = int(np.count_nonzero(tied))
     # weights matched by expert id on tokens with identical sets
     og = np.argsort(gpu_ids[same], 1)
     oo = np.argsort(oids[same], 1)

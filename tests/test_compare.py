@@ -101,3 +101,10 @@ def test_per_token_rel_err():
     ref = np.array([[1.0, -2.0], [0.01, 0.0]])
     got = np.array([[1.0, -2.02], [0.0101, 0.0]], np.float32)
     assert abs(gu.per_token_rel_err(got, ref) - 0.01) < 1e-6
+
+
+def test_exact_ties_counted_once_per_token():
+    # equal keys inside the set and at the cut: one token
+    ref = _case([[0.7, 0.7, 0.7, 0.1]])
+    rep = gu.compare_route(WL, ref["ids"].copy(), ref["w"].astype(np.float32), ref)
+    assert rep.exact_ties == 1
