@@ -122,11 +122,14 @@ def compare_route(wl, gpu_ids, gpu_w, ref) -> RouteReport:
     """Ids and gating weights of the GPU against ref = oracle.route(...,
     want_keys=True), token by token.
 
-    * Set: equal to the oracle's, unless the oracle's k-th and (k+1)-th keys
-      differ by a nonzero amount below GAP_TOL (a near-tie, which fp32 may
-      resolve either way).  Then the GPU's set must still be a valid top-k
-      within GAP_TOL.  Equal keys rank the lower expert index first on both
-      sides, so an exact tie at the cut is not exempt: the ids must match.
+    * Set: equal to the oracle's, unless the token is a near-tie: an expert
+      in the oracle's set and one outside it have keys that differ by a
+      nonzero amount below GAP_TOL, which fp32 may order either way (the
+      oracle's k-th and (k+1)-th keys closer than GAP_TOL but not equal, or
+      equal with another expert within GAP_TOL of them).  Then the GPU's set
+      must still be a valid top-k within GAP_TOL.  Equal keys rank the lower
+      expert index first on both sides, so an exact tie at the cut with no
+      such neighbour is not exempt: the ids must match.
     * Rank order: slot by slot the GPU's id equals the oracle's, unless the
       two experts' oracle keys differ by a nonzero amount below GAP_TOL.
       Along the GPU's slots the oracle keys never increase by GAP_TOL or
@@ -139,7 +142,14 @@ def compare_route(wl, gpu_ids, gpu_w, ref) -> RouteReport:
     keys = ref["keys"]
     gap = ref["gap"]
     assert np.all((gpu_ids >= 0) & (gpu_ids < keys.shape[1])), "expert id out of range"
-    near = np.nonzero((gap > 0) & (gap < GAP_TOL))[0]
+    kth = np.take_along_axis(keys, oids[:, -1:].astype(np.int64), 1)[:, 0]  # oracle's cut key
+    near_mask = (gap > 0) & (gap < GAP_TOL)
+    if np.any(gap == 0):
+        # exact tie at the cut: a near-tie only if another key lies within
+        # GAP_TOL of the cut key without being equal to it
+        close = (np.abs(keys - kth[:, None]) < GAP_TOL) & (keys != kth[:, None])
+        near_mask |= (gap == 0) & np.any(close, 1)
+    near = np.nonzero(near_mask)[0]
     mism = np.nonzero(np.any(np.sort(gpu_ids, 1) != np.sort(oids, 1), 1))[0]
     bad = np.setdiff1d(mism, near)
     assert bad.size == 0, f"expert ids differ on tokens that are not near-ties {bad[:10].tolist()}"

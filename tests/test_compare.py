@@ -108,3 +108,18 @@ def test_exact_ties_counted_once_per_token():
     ref = _case([[0.7, 0.7, 0.7, 0.1]])
     rep = gu.compare_route(WL, ref["ids"].copy(), ref["w"].astype(np.float32), ref)
     assert rep.exact_ties == 1
+
+
+def test_exact_tie_at_the_cut_with_a_near_neighbour_is_exempt():
+    # experts 2 and 3 tie exactly at the cut (top 2: 0 and 2); expert 1 is
+    # 1e-8 above them, so fp32 may rank 1 below the tied pair: {0, 2} and
+    # {0, 1} are both valid sets
+    ref = _case([[0.9, 0.4 + 1e-8, 0.4, 0.4]], k=3)
+    assert ref["ids"].tolist() == [[0, 1, 2]] and ref["gap"][0] == 0.0
+    rep = gu.compare_route(WL, np.array([[0, 2, 3]], np.int32), np.full((1, 3), 1.0, np.float32),
+                           ref)
+    assert rep.mismatched == [0] and rep.near_tie == [0]
+    # the tied pair itself must still come lower index first
+    with pytest.raises(AssertionError):
+        gu.compare_route(WL, np.array([[0, 3, 2]], np.int32), np.full((1, 3), 1.0, np.float32),
+                         ref)
