@@ -30,7 +30,9 @@
  *     router_w [E][H] (fp32), router_bias [E] (fp32).
  *   - Pair id p = t * k + j names slot j of token t.
  *   - The caller owns every buffer.  The library allocates no device memory
- *     and keeps no state between calls except the per-thread error text.
+ *     and keeps no state between calls except the per-thread error text and
+ *     the fixed scratch of moe_forward_noalloc (a device array per GPU, sized
+ *     at build time, allocated by the runtime when the library is loaded).
  *   - Every call only enqueues work on `stream` (0 = the null stream) and
  *     returns without synchronising; results are ready when the stream is.
  *   - Arguments are validated before anything is enqueued: an error return
@@ -203,6 +205,32 @@ moe_status moe_forward_fused(const moe_config* cfg, const uint16_t* x, const flo
                              const uint16_t* ws_gate, const uint16_t* ws_up,
                              const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
                              float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- Layer forward that allocates nothing ----------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same forward as moe_forward (same kernels, same results bit
+ * for bit), with its workspace in a fixed scratch array inside the library:
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory on each GPU the
+ * library runs on, held from the library's load there until the process
+ * ends.  That covers the full-shape layer (hidden 4096, 288 experts, top 8,
+ * intermediate 1280) up to about 630 tokens; a configuration whose
+ * moe_workspace_size() exceeds it returns MOE_ERR_WORKSPACE before anything
+ * is enqueued.  The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); on its first call on a device it looks up
+ * that device's scratch address.
+ * Every call on one GPU uses that GPU's one scratch array, which keeps the
+ * last call's contents (each call writes what it reads first): calls that
+ * overlap on one GPU -- on different streams or host threads without
+ * ordering -- race on it and must not be issued.  Arguments, outputs and
+ * errors are those of moe_forward; no workspace argument. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_config* cfg, const uint16_t* x, const float* router_w,
+                               const float* router_bias, const uint16_t* w_gate,
+                               const uint16_t* w_up, const uint16_t* w_down,
+                               const uint16_t* ws_gate, const uint16_t* ws_up,
+                               const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
+                               float* topk_w_out, hipStream_t stream);
 
 /* Where an intermediate of moe_forward lives inside the workspace, for
  * inspection after the stream has finished (tests, debugging).  Writes the

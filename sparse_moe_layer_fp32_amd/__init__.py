@@ -78,6 +78,7 @@ def load_library():
     lib.moe_permute.argtypes = [cp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_forward.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_forward_timed.argtypes = lib.moe_forward.argtypes + [ctypes.POINTER(vp), ctypes.c_int]
+    lib.moe_forward_noalloc.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_workspace_view.argtypes = [cp, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.moe_forward_fp8.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, sz, vp]
@@ -95,7 +96,9 @@ def load_library():
 
 EXPORTED = ("moe_workspace_size", "moe_last_error", "moe_route", "moe_permute", "moe_forward",
             "moe_forward_timed", "moe_workspace_view", "moe_dense_workspace_size",
-            "moe_dense_forward", "moe_forward_fp8", "moe_forward_fused")
+            "moe_dense_forward", "moe_forward_fp8", "moe_forward_fused",
+            "moe_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 
 # ------------------------------------------------------------------ helpers
@@ -185,16 +188,18 @@ def moe_permute(cfg, topk_ids, expert_offsets, sorted_pairs, pair_pos, ws, strea
 
 
 def _forward_args(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                  y, topk_ids_out, topk_w_out, ws, stream):
+                  y, topk_ids_out, topk_w_out, ws, stream, no_ws=False):
     bf = _bf16()
-    return [ctypes.byref(cfg), _ptr(x, bf, "x"), _ptr(router_w, _f32(), "router_w"),
+    args = [ctypes.byref(cfg), _ptr(x, bf, "x"), _ptr(router_w, _f32(), "router_w"),
             _ptr(router_bias, _f32(), "router_bias", True), _ptr(w_gate, bf, "w_gate"),
             _ptr(w_up, bf, "w_up"), _ptr(w_down, bf, "w_down"),
             _ptr(ws_gate, bf, "ws_gate", True), _ptr(ws_up, bf, "ws_up", True),
             _ptr(ws_down, bf, "ws_down", True), _ptr(y, bf, "y"),
             _ptr(topk_ids_out, _i32(), "topk_ids_out", True),
-            _ptr(topk_w_out, _f32(), "topk_w_out", True), _ptr(ws, None, "ws"),
-            ws.numel() * ws.element_size(), _stream(stream)]
+            _ptr(topk_w_out, _f32(), "topk_w_out", True)]
+    if not no_ws:
+        args += [_ptr(ws, None, "ws"), ws.numel() * ws.element_size()]
+    return args + [_stream(stream)]
 
 
 def moe_forward(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
@@ -212,6 +217,16 @@ def moe_forward_fused(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_ga
     _check(lib.moe_forward_fused(*_forward_args(cfg, x, router_w, router_bias, w_gate, w_up,
                                                 w_down, ws_gate, ws_up, ws_down, y, topk_ids_out,
                                                 topk_w_out, ws, stream)))
+
+
+def moe_forward_noalloc(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                        ws_down, y, topk_ids_out=None, topk_w_out=None, stream=None):
+    """moe_forward with the library's fixed scratch as its workspace (no
+    workspace argument, nothing allocated)."""
+    lib = load_library()
+    args = _forward_args(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                         ws_down, y, topk_ids_out, topk_w_out, None, stream, no_ws=True)
+    _check(lib.moe_forward_noalloc(*args))
 
 
 def moe_forward_timed(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up,

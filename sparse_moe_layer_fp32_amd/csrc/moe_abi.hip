@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -236,12 +237,15 @@ struct Fp8Weights {
   const float *s_gate, *s_up, *s_down;
 };
 
-moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* router_w,
-                        const float* router_bias, const uint16_t* w_gate, const uint16_t* w_up,
-                        const uint16_t* w_down, const uint16_t* ws_gate, const uint16_t* ws_up,
-                        const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
-                        float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                        hipEvent_t* ev, const Fp8Weights* f8 = nullptr) {
+// The configuration and the pointers of a layer forward (bf16 or, with f8,
+// e4m3 routed weights), before anything else.
+moe_status check_forward_args(const moe_config* c, const uint16_t* x, const float* router_w,
+                              const float* router_bias, const uint16_t* w_gate,
+                              const uint16_t* w_up, const uint16_t* w_down,
+                              const uint16_t* ws_gate, const uint16_t* ws_up,
+                              const uint16_t* ws_down, const uint16_t* y,
+                              const int32_t* topk_ids_out, const float* topk_w_out,
+                              const Fp8Weights* f8) {
   moe_status st = validate(c);
   if (st) return st;
   const bool routed_ok = f8 ? (f8->gate && f8->up && f8->down && f8->s_gate && f8->s_up &&
@@ -258,6 +262,18 @@ moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* rou
                         f8 ? f8->s_down : nullptr};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(MOE_ERR_UNSUPPORTED, "pointer %p not 16-byte aligned", q);
+  return MOE_OK;
+}
+
+moe_status forward_impl(const moe_config* c, const uint16_t* x, const float* router_w,
+                        const float* router_bias, const uint16_t* w_gate, const uint16_t* w_up,
+                        const uint16_t* w_down, const uint16_t* ws_gate, const uint16_t* ws_up,
+                        const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
+                        float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                        hipEvent_t* ev, const Fp8Weights* f8 = nullptr) {
+  moe_status st = check_forward_args(c, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate,
+                                     ws_up, ws_down, y, topk_ids_out, topk_w_out, f8);
+  if (st) return st;
   Plan p;
   make_plan(c, &p);
   if ((st = check_ws(p, ws, ws_bytes))) return st;
@@ -388,6 +404,40 @@ void make_dense_plan(const moe_dense_config* c, DensePlan* p) {
   p->queue = take(moe::kQueueWords * 4);
   p->h = take(static_cast<size_t>(p->T) * p->I * 2);
   p->total = off;
+}
+
+// ---- fixed scratch of moe_forward_noalloc.
+// The workspace of moe_forward (router partials, permutation, GEMM tile
+// lists and queue counters, h and o) lives in this file-scope device array
+// instead of caller memory.  Each device holds its own copy, allocated by the
+// runtime when the library's code object is loaded there, for the life of the
+// process.  Host code never names the array for its memory: its device
+// address is taken once per device with hipGetSymbolAddress and kept here.
+static_assert(MOE_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use).
+moe_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the %d devices with a scratch slot", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -544,6 +594,29 @@ moe_status moe_forward_fused(const moe_config* cfg, const uint16_t* x, const flo
                              float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   return forward_fused_impl(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up,
                             ws_down, y, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, const uint16_t* x, const float* router_w,
+                               const float* router_bias, const uint16_t* w_gate,
+                               const uint16_t* w_up, const uint16_t* w_down,
+                               const uint16_t* ws_gate, const uint16_t* ws_up,
+                               const uint16_t* ws_down, uint16_t* y, int32_t* topk_ids_out,
+                               float* topk_w_out, hipStream_t stream) {
+  moe_status st = check_forward_args(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate,
+                                     ws_up, ws_down, y, topk_ids_out, topk_w_out, nullptr);
+  if (st) return st;
+  Plan p;
+  make_plan(cfg, &p);
+  if (p.total > static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES))
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: this batch needs %zu bytes of workspace, the fixed scratch "
+                "holds %zu (use moe_forward with a caller workspace)",
+                p.total, static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+  if (p.T == 0) return ok();
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return forward_impl(cfg, x, router_w, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                      y, topk_ids_out, topk_w_out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 moe_status moe_workspace_view(const moe_config* cfg, int which, size_t* offset, size_t* bytes) {

@@ -173,3 +173,24 @@ def test_fused_errors_before_launch():
     s_off, s_nb = moe.moe_workspace_view(cfg, moe.MOE_WS_FUSED_STATUS)
     assert c_off + c_nb <= total and c_nb % 256 == 0 and s_nb == 4
     assert c_off <= s_off < c_off + c_nb
+
+
+def test_noalloc_errors_before_launch():
+    """moe_forward_noalloc: a batch whose workspace exceeds the fixed scratch
+    and NULL pointers are refused before anything is enqueued (no device
+    call); an empty batch returns at once."""
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    args = [fake, fake, None, fake, fake, fake, fake, fake, fake, fake, None, None]
+    big = full(1024)
+    assert moe.moe_workspace_size(big) > moe.NOALLOC_SCRATCH_BYTES
+    st = lib.moe_forward_noalloc(ctypes.byref(big), *args, None)
+    assert st == moe.MOE_ERR_WORKSPACE and "scratch" in moe.moe_last_error()
+    st = lib.moe_forward_noalloc(ctypes.byref(full(64)), None, *args[1:], None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    st = lib.moe_forward_noalloc(ctypes.byref(full(64)), mis, *args[1:], None)
+    assert st == moe.MOE_ERR_UNSUPPORTED
+    st = lib.moe_forward_noalloc(ctypes.byref(full(0)), None, *args[1:10], None, None, None, None)
+    assert st == moe.MOE_OK
+    assert moe.moe_workspace_size(full(630)) <= moe.NOALLOC_SCRATCH_BYTES
