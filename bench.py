@@ -2,10 +2,17 @@
 
 One step = one full layer forward (router, top-k, permutation, grouped
 gate/up and down GEMMs with the shared expert, combine) over one batch of
-synthetic tokens, inputs already resident in HBM.  The default workload is
-the full-shape decode layer (T = 64 tokens, hidden 4096, 288 experts top-8,
-intermediate 1280, shared expert); the full-shape prefill layer (T = 8192)
-is measured beside it and reported under "prefill".
+synthetic tokens, inputs already resident in HBM.
+
+The headline (``value``) is the full-shape decode layer (T = 64 tokens,
+hidden 4096, 288 experts top-8, intermediate 1280, shared expert): exactly
+--steps steps after --warmup, wall clock between device synchronisations.
+Beside it, every workload -- tiny, decode, prefill (T 8192), skewed (T 4096,
+clamp 7.0), long (T 32768), and decode and prefill with no router bias as
+supplements -- is timed with HIP events per step over fixed counts (5
+warm-up steps, then 100 steps for tiny and decode, 20 for the others) and
+reported under "configs" / "supplements" with the median, p10 and p90, the
+rates, the roofline fractions and the routing the run produced.
 
 Each step reads the routed weights of another copy of the layer (weight
 copies rotate), as consecutive MoE layers of a model would, so the 256 MB
@@ -49,10 +56,12 @@ def parse():
     ap.add_argument("--config", default="decode",
                     choices=["decode", "prefill", "skewed", "long", "tiny"])
     ap.add_argument("--weight-copies", type=int, default=4)
-    ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time the --config workload only (no other workloads or supplements)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the second workloads (Step-3 MoE shape, dense FFN)")
+                    help="skip the second workloads (single launch, Step-3 MoE shape, FP8, "
+                         "dense FFN)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES five times (to scale HBM "
                          "traffic counters) and exit")
@@ -63,24 +72,37 @@ def parse():
 
 
 # Commands whose outputs --summarize-profiles reads (DIR = its argument).
-PROFILE_COMMANDS = {
-    "kt_decode": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/kt_decode -o run -- "
-                 "python3 bench.py --config decode --steps 20 --warmup 5 --no-cpu --no-secondary",
-    "kt_prefill": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/kt_prefill -o run -- "
-                  "python3 bench.py --config prefill --steps 10 --warmup 3 --no-cpu --weight-copies 2",
-    "pmc_fetch_decode": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch_decode -o run -- "
-                        "python3 bench.py --config decode --steps 4 --warmup 1 --no-cpu --no-secondary",
-    "pmc_write_decode": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write_decode -o run -- "
-                        "python3 bench.py --config decode --steps 4 --warmup 1 --no-cpu --no-secondary",
-    "pmc_fetch_prefill": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch_prefill -o run -- "
-                         "python3 bench.py --config prefill --steps 2 --warmup 1 --no-cpu --weight-copies 1",
-    "pmc_write_prefill": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write_prefill -o run -- "
-                         "python3 bench.py --config prefill --steps 2 --warmup 1 --no-cpu --weight-copies 1",
-    "pmc_fetch_copy": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch_copy -o run -- "
-                      "python3 bench.py --copy-calibration 1073741824",
-    "pmc_write_copy": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write_copy -o run -- "
-                      "python3 bench.py --copy-calibration 1073741824",
-}
+_B = "python3 bench.py --no-cpu --only-headline"
+_RUNS = {"decode": "--config decode --steps 20 --warmup 5",
+         "prefill": "--config prefill --steps 10 --warmup 3 --weight-copies 2",
+         "skewed": "--config skewed --steps 10 --warmup 3 --weight-copies 2",
+         "long": "--config long --steps 5 --warmup 2 --weight-copies 2"}
+_SHORT = {"decode": "--config decode --steps 4 --warmup 1",
+          "prefill": "--config prefill --steps 2 --warmup 1 --weight-copies 1",
+          "skewed": "--config skewed --steps 2 --warmup 1 --weight-copies 1",
+          "long": "--config long --steps 2 --warmup 1 --weight-copies 1"}
+MFMA_COUNTERS = "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE"
+PROFILE_COMMANDS = {}
+for _w in _RUNS:
+    PROFILE_COMMANDS[f"kt_{_w}"] = (
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/kt_{_w} -o run -- "
+        f"{_B} {_RUNS[_w]}")
+for _w in ("prefill", "skewed", "long"):
+    PROFILE_COMMANDS[f"pmc_mfma_{_w}"] = (
+        f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv "
+        f"-d DIR/pmc_mfma_{_w} -o run -- {_B} {_SHORT[_w]}")
+    PROFILE_COMMANDS[f"pmc_l2_{_w}"] = (
+        f"rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d DIR/pmc_l2_{_w} -o run "
+        f"-- {_B} {_SHORT[_w]}")
+for _w in ("decode", "prefill", "skewed", "long"):
+    for _c in ("FETCH_SIZE", "WRITE_SIZE"):
+        _k = f"pmc_{_c.split('_')[0].lower()}_{_w}"
+        PROFILE_COMMANDS[_k] = (f"rocprofv3 --pmc {_c} --output-format csv -d DIR/{_k} -o run -- "
+                                f"{_B} {_SHORT[_w]}")
+for _c in ("FETCH_SIZE", "WRITE_SIZE"):
+    _k = f"pmc_{_c.split('_')[0].lower()}_copy"
+    PROFILE_COMMANDS[_k] = (f"rocprofv3 --pmc {_c} --output-format csv -d DIR/{_k} -o run -- "
+                            "python3 bench.py --copy-calibration 1073741824")
 # The sources each kernel is built from (its file and the headers it includes).
 _EXPERT_SRC = ("experts.hip", "expert_tile.h", "common.h", "kernels.h")
 _ROUTER_SRC = ("router.hip", "router_ops.h", "common.h", "kernels.h")
@@ -106,18 +128,29 @@ def _src_sha(fnames):
     return h.hexdigest()
 
 
+def _kernel_key(short):
+    base = short.split("<")[0]
+    mode = re.match(r"expert_gemm(?:_persistent)?<(\d)", short)
+    if mode:
+        return {"0": "gateup_kernel", "1": "down_kernel", "2": "router_logits_kernel"}[mode.group(1)]
+    return base
+
+
 def summarize_profiles(d):
-    """Turn rocprofv3 CSV outputs under d (made by PROFILE_COMMANDS) into the
-    text summaries under profiles/ and profiles/traffic.json."""
+    """Turn the rocprofv3 CSV outputs under d (made by PROFILE_COMMANDS; any
+    subset) into the text summaries under profiles/ and profiles/traffic.json."""
     import csv
     import collections
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
-    for wl in ("decode", "prefill"):
-        path = os.path.join(d, f"kt_{wl}", "run_kernel_stats.csv")
-        rows = list(csv.DictReader(open(path)))
+    have = lambda k: os.path.isdir(os.path.join(d, k))  # noqa: E731
+    wrote = []
+    for wl in _RUNS:
+        if not have(f"kt_{wl}"):
+            continue
+        rows = list(csv.DictReader(open(os.path.join(d, f"kt_{wl}", "run_kernel_stats.csv"))))
         lines = [f"# Kernel durations, {wl} workload (rocprofv3 kernel trace)", "",
-                 "Command (from /tmp with TMPDIR=/tmp; DIR = an output directory):", "",
+                 "Command (run from the repository root with TMPDIR=/tmp; DIR = an output directory):", "",
                  "```", PROFILE_COMMANDS[f"kt_{wl}"], "```", "",
                  "| Kernel | Calls | Average us | Min us | Max us | Share |",
                  "|---|---|---|---|---|---|"]
@@ -125,54 +158,117 @@ def summarize_profiles(d):
             lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                          f"{float(r['Percentage']):.1f}% |")
-        lines += ["", "`__amd_rocclr_copyBuffer` is the benchmark's own weight-copy setup, outside "
-                  "the timed region.", ""]
+        lines += ["", "`__amd_rocclr_copyBuffer` and the fill kernels are the benchmark's own "
+                  "weight-copy and buffer set-up, outside the timed region.", ""]
         with open(os.path.join(out_dir, f"kernels_{wl}.md"), "w") as f:
             f.write("\n".join(lines))
+        wrote.append(f"kernels_{wl}.md")
 
-    def per_kernel(name):
-        agg = collections.defaultdict(list)
+    def counters(name):
+        """{kernel: {counter: mean value per dispatch}}"""
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
         for r in csv.DictReader(open(os.path.join(d, name, "run_counter_collection.csv"))):
-            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+            agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+
+    def durations(name):
+        """{kernel: mean duration in ns} from the kernel trace of the same run."""
+        path = os.path.join(d, name, "run_kernel_trace.csv")
+        agg = collections.defaultdict(list)
+        if os.path.exists(path):
+            for r in csv.DictReader(open(path)):
+                agg[r["Kernel_Name"]].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
         return {k: sum(v) / len(v) for k, v in agg.items()}
 
-    copy_fetch = per_kernel("pmc_fetch_copy")["__amd_rocclr_copyBuffer"]
-    copy_write = per_kernel("pmc_write_copy")["__amd_rocclr_copyBuffer"]
-    cal_bytes = 1073741824
-    f_fetch = cal_bytes / (copy_fetch * 1024)   # bytes per reported KiB unit
-    f_write = cal_bytes / (copy_write * 1024)
-    traffic = {"calibration": {"copy_bytes": cal_bytes, "fetch_kib": copy_fetch,
-                               "write_kib": copy_write, "fetch_factor": f_fetch,
-                               "write_factor": f_write}}
-    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
-             "Each counter ran alone.  Scale: a plain 1 GiB device copy "
-             f"(`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = {copy_fetch:.0f} KiB and "
-             f"WRITE_SIZE = {copy_write:.0f} KiB, so bytes = FETCH_SIZE x 1024 x {f_fetch:.3f} "
-             f"and WRITE_SIZE x 1024 x {f_write:.3f}.", "", "Commands (from /tmp with TMPDIR=/tmp):", "", "```"]
-    lines += [PROFILE_COMMANDS[k] for k in PROFILE_COMMANDS if k.startswith("pmc_")]
-    lines += ["```", "", "| Workload | Kernel | Read MB/launch | Written MB/launch |", "|---|---|---|---|"]
-    for wl in ("decode", "prefill"):
-        fe = per_kernel(f"pmc_fetch_{wl}")
-        wr = per_kernel(f"pmc_write_{wl}")
-        for k in sorted(fe, key=lambda k: -fe[k]):
+    for wl in ("prefill", "skewed", "long"):
+        if not have(f"pmc_mfma_{wl}"):
+            continue
+        cs, du = counters(f"pmc_mfma_{wl}"), durations(f"pmc_mfma_{wl}")
+        lines = [f"# MFMA utilisation, {wl} workload (rocprofv3 counters)", "",
+                 "Command (run from the repository root with TMPDIR=/tmp; DIR = an output directory):", "", "```",
+                 PROFILE_COMMANDS[f"pmc_mfma_{wl}"], "```", "",
+                 "MfmaUtil is rocprofv3's derived counter: the MFMA units' busy cycles summed "
+                 "over the SIMDs, over the GPU's active cycles times the SIMD count.  Issued "
+                 "bf16 MFMA work is SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP (padding rows "
+                 "included).  The clock is GRBM_GUI_ACTIVE over the kernel's duration in the "
+                 "same run.", "",
+                 "| Kernel | MfmaUtil % | Issued bf16 TFLOP/launch | Duration us | Clock GHz | "
+                 "Issued TFLOP/s |", "|---|---|---|---|---|---|"]
+        for k in sorted(cs, key=lambda k: -cs[k].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0)):
             if "moe::" not in k:
                 continue
-            rb = fe[k] * 1024 * f_fetch
-            wb = wr.get(k, 0.0) * 1024 * f_write
-            lines.append(f"| {wl} | `{_short(k)}` | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
-            short = _short(k)
-            base = short.split("<")[0]
-            mode = re.match(r"expert_gemm(?:_persistent)?<(\d)", short)
-            key = ("gateup_kernel" if mode and mode.group(1) == "0" else
-                   "down_kernel" if mode and mode.group(1) == "1" else base)
-            traffic[f"{key}:{wl}"] = {"kernel": short, "read_bytes": rb, "write_bytes": wb,
-                                      "bytes_per_launch": rb + wb,
-                                      "source_sha256": _src_sha(KERNEL_SOURCES.get(base, _EXPERT_SRC))}
-    with open(os.path.join(out_dir, "hbm_traffic.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
-    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
-        json.dump(traffic, f, indent=1)
-    print(f"wrote {out_dir}")
+            c = cs[k]
+            fl = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+            dur = du.get(k)
+            clk = c.get("GRBM_GUI_ACTIVE", 0.0) / dur if dur else float("nan")
+            rate = fl / (dur * 1e-9) * 1e-12 if dur else float("nan")
+            lines.append(f"| `{_short(k)}` | {c.get('MfmaUtil', float('nan')):.1f} | {fl * 1e-12:.4f} | "
+                         f"{dur / 1e3 if dur else float('nan'):.1f} | {clk:.3f} | {rate:.1f} |")
+        with open(os.path.join(out_dir, f"mfma_{wl}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        wrote.append(f"mfma_{wl}.md")
+
+    l2 = [wl for wl in ("prefill", "skewed", "long") if have(f"pmc_l2_{wl}")]
+    if l2:
+        lines = ["# L2 hit rate (rocprofv3 TCC_HIT_sum / TCC_MISS_sum)", "",
+                 "Commands (run from the repository root with TMPDIR=/tmp; DIR = an output directory):", "", "```"]
+        lines += [PROFILE_COMMANDS[f"pmc_l2_{wl}"] for wl in l2]
+        lines += ["```", "", "| Workload | Kernel | L2 hits / launch | L2 misses / launch | Hit rate |",
+                  "|---|---|---|---|---|"]
+        for wl in l2:
+            cs = counters(f"pmc_l2_{wl}")
+            for k in sorted(cs, key=lambda k: -cs[k].get("TCC_MISS_sum", 0)):
+                if "moe::" not in k:
+                    continue
+                h, m = cs[k].get("TCC_HIT_sum", 0.0), cs[k].get("TCC_MISS_sum", 0.0)
+                lines.append(f"| {wl} | `{_short(k)}` | {h:.3e} | {m:.3e} | "
+                             f"{h / (h + m) if h + m else 0:.3f} |")
+        with open(os.path.join(out_dir, "l2_hits.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        wrote.append("l2_hits.md")
+
+    if have("pmc_fetch_copy") and have("pmc_write_copy"):
+        copy_fetch = counters("pmc_fetch_copy")["__amd_rocclr_copyBuffer"]["FETCH_SIZE"]
+        copy_write = counters("pmc_write_copy")["__amd_rocclr_copyBuffer"]["WRITE_SIZE"]
+        cal_bytes = 1073741824
+        f_fetch = cal_bytes / (copy_fetch * 1024)   # bytes per reported KiB unit
+        f_write = cal_bytes / (copy_write * 1024)
+        traffic = {"calibration": {"copy_bytes": cal_bytes, "fetch_kib": copy_fetch,
+                                   "write_kib": copy_write, "fetch_factor": f_fetch,
+                                   "write_factor": f_write}}
+        wls = [wl for wl in _RUNS if have(f"pmc_fetch_{wl}") and have(f"pmc_write_{wl}")]
+        lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+                 "Each counter ran alone.  Scale: a plain 1 GiB device copy "
+                 f"(`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = {copy_fetch:.0f} KiB and "
+                 f"WRITE_SIZE = {copy_write:.0f} KiB, so bytes = FETCH_SIZE x 1024 x {f_fetch:.3f} "
+                 f"and WRITE_SIZE x 1024 x {f_write:.3f}.  The counters count what the L2 "
+                 "requests from memory, last-level (MALL) hits included.", "",
+                 "Commands (run from the repository root with TMPDIR=/tmp; DIR = an output directory):", "", "```"]
+        lines += [PROFILE_COMMANDS[f"pmc_{c}_{wl}"] for wl in wls + ["copy"]
+                  for c in ("fetch", "write")]
+        lines += ["```", "", "| Workload | Kernel | Read MB/launch | Written MB/launch |",
+                  "|---|---|---|---|"]
+        for wl in wls:
+            fe = {k: v["FETCH_SIZE"] for k, v in counters(f"pmc_fetch_{wl}").items()}
+            wr = {k: v["WRITE_SIZE"] for k, v in counters(f"pmc_write_{wl}").items()}
+            for k in sorted(fe, key=lambda k: -fe[k]):
+                if "moe::" not in k:
+                    continue
+                rb = fe[k] * 1024 * f_fetch
+                wb = wr.get(k, 0.0) * 1024 * f_write
+                short = _short(k)
+                lines.append(f"| {wl} | `{short}` | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+                base = short.split("<")[0]
+                traffic[f"{_kernel_key(short)}:{wl}"] = {
+                    "kernel": short, "read_bytes": rb, "write_bytes": wb,
+                    "bytes_per_launch": rb + wb,
+                    "source_sha256": _src_sha(KERNEL_SOURCES.get(base, _EXPERT_SRC))}
+        with open(os.path.join(out_dir, "hbm_traffic.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+            json.dump(traffic, f, indent=1)
+        wrote += ["hbm_traffic.md", "traffic.json"]
+    print(f"wrote {', '.join(wrote)} under {out_dir}")
 
 
 def copy_calibration(nbytes):
@@ -215,221 +311,292 @@ def traffic_for(kernel, workload):
     return ent.get("bytes_per_launch")
 
 
-def measure(wl, moe, synth, experts_host, copies, steps, warmup):
+def _dev(a):
     import numpy as np
     import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
 
-    def dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(a).cuda()
 
-    x = dev(synth.gen_x(wl))
-    rw_h, rb_h, _ = synth.gen_router(wl)
-    rw, rb = dev(rw_h), (dev(rb_h) if wl.use_bias else None)
-    cfg = moe.make_config(wl.T, wl.H, wl.E, wl.k, wl.I, wl.Is, wl.routed_scaling,
-                          wl.renormalize, wl.limit, wl.limit_shared)
-    ws = moe.alloc_workspace(cfg)
-    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
-    ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
-    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+def _pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v), q))
 
-    def step(i, events=None):
-        c = copies[i % len(copies)]
-        if events is None:
-            moe.moe_forward(cfg, x, rw, rb, *c, y, ids, w, ws)
-        else:
-            moe.moe_forward_timed(cfg, x, rw, rb, *c, y, ids, w, ws, events=events)
 
+def time_steps(step, warmup, steps):
+    """Per-step GPU time in ms: HIP events recorded on the launch stream (the
+    current stream, where the library enqueues) around each step; the steps
+    are enqueued back to back after `warmup` untimed ones."""
+    import torch
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
     for i in range(steps):
+        evs[i][0].record()
         step(i)
+        evs[i][1].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / steps
+    return [a.elapsed_time(b) for a, b in evs]
 
-    # Per-kernel durations: the same steps again with HIP events recorded on
-    # the launch stream between the kernels.
-    nst = moe.MOE_NUM_STAGES
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
-    for i in range(steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    stage_ms = {name: sum(e[s].elapsed_time(e[s + 1]) for e in evs) / steps
-                for s, name in enumerate(moe.STAGES)}
 
-    ids_h = ids.cpu().numpy()
+class Layer:
+    """Device inputs of one workload: x, the router and a list of weight
+    copies (steps rotate through them)."""
+
+    def __init__(self, wl, moe, synth, copies, use_bias=True):
+        import torch
+        self.wl, self.moe = wl, moe
+        self.x_host = synth.gen_x(wl)
+        self.rw_host, rb_host, _ = synth.gen_router(wl)
+        self.rb_host = rb_host if (wl.use_bias and use_bias) else None
+        self.x = _dev(self.x_host)
+        self.rw = _dev(self.rw_host)
+        self.rb = None if self.rb_host is None else _dev(self.rb_host)
+        self.copies = copies
+        self.cfg = moe.make_config(wl.T, wl.H, wl.E, wl.k, wl.I, wl.Is, wl.routed_scaling,
+                                   wl.renormalize, wl.limit, wl.limit_shared)
+        self.ws = moe.alloc_workspace(self.cfg)
+        self.y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+        self.ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+
+    def step(self, i, events=None):
+        c = self.copies[i % len(self.copies)]
+        if events is None:
+            self.moe.moe_forward(self.cfg, self.x, self.rw, self.rb, *c, self.y, self.ids, self.w,
+                                 self.ws)
+        else:
+            self.moe.moe_forward_timed(self.cfg, self.x, self.rw, self.rb, *c, self.y, self.ids,
+                                       self.w, self.ws, events=events)
+
+    def stage_ms(self, steps):
+        """Per-kernel mean durations from events recorded between the kernels."""
+        import torch
+        nst = self.moe.MOE_NUM_STAGES
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+               for _ in range(steps)]
+        for i in range(steps):
+            self.step(i, evs[i])
+        torch.cuda.synchronize()
+        return {name: sum(e[s].elapsed_time(e[s + 1]) for e in evs) / steps
+                for s, name in enumerate(self.moe.STAGES)}
+
+    def free(self):
+        del self.ws, self.y, self.x
+
+
+def summarize(wl, ms, stage, ids_h):
+    """One record of a timed workload: times, rates, roofline fractions and
+    the routing the run produced."""
+    import numpy as np
     hist = np.bincount(ids_h.ravel(), minlength=wl.E)
     U = int(np.count_nonzero(hist))
     c = counts(wl, U)
-    t = ms * 1e-3
-    gu_t = stage_ms["gateup"] * 1e-3
-    out = dict(
-        ms_per_step=ms,
-        tokens_per_s=wl.T / t,
-        tflops=(c["flop_router"] + c["flop_experts"]) / t * 1e-12,
-        gbs=c["bytes_layer"] / t * 1e-9,
-        frac_mfma=(c["flop_router"] + c["flop_experts"]) / t * 1e-12 / BF16_PEAK_TFLOPS,
-        frac_hbm=c["bytes_layer"] / t * 1e-9 / HBM_PEAK_GBS,
-        stage_ms={k: round(v, 5) for k, v in stage_ms.items()},
-        experts_used=U,
-        tokens_per_expert=dict(min=int(hist.min()), median=float(np.median(hist)),
-                               max=int(hist.max())),
-        hot16_share=float(np.sort(hist)[::-1][:16].sum() / hist.sum()),
-        gateup=dict(ms=stage_ms["gateup"], gbs=c["gateup_bytes"] / gu_t * 1e-9,
-                    tflops=c["gateup_flop"] / gu_t * 1e-12, bytes=c["gateup_bytes"],
-                    flop=c["gateup_flop"]),
+    med = _pct(ms, 50) * 1e-3
+    flop = c["flop_router"] + c["flop_experts"]
+    flop_fp32 = c["flop_router"]
+    tfl = flop / med * 1e-12
+    gbs = c["bytes_layer"] / med * 1e-9
+    gu_t = stage["gateup"] * 1e-3
+    bound = "hbm" if gbs / HBM_PEAK_GBS > tfl / BF16_PEAK_TFLOPS else "mfma"
+    # time the work needs at the peaks: bf16 FLOPs at the MFMA peak plus the
+    # fp32 router FLOPs at the fp32 peak, or the bytes at the HBM peak
+    ideal = max((flop - flop_fp32) / (BF16_PEAK_TFLOPS * 1e12) + flop_fp32 / (FP32_PEAK_TFLOPS * 1e12),
+                c["bytes_layer"] / (HBM_PEAK_GBS * 1e9))
+    return dict(
+        tokens=wl.T, seed=wl.seed, swiglu_limit=wl.limit, router_bias=wl.use_bias,
+        ms=dict(median=round(_pct(ms, 50), 5), p10=round(_pct(ms, 10), 5),
+                p90=round(_pct(ms, 90), 5), steps=len(ms)),
+        tokens_per_s=round(wl.T / med, 1), tflops=round(tfl, 2), gbs=round(gbs, 1),
+        frac_mfma=round(tfl / BF16_PEAK_TFLOPS, 4), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
+        roofline_frac=round(ideal / med, 4), bound=bound,
+        algorithmic=dict(flop=flop, bytes=c["bytes_layer"]),
+        stage_ms={k: round(v, 5) for k, v in stage.items()},
+        gateup=dict(ms=round(stage["gateup"], 5),
+                    gbs=round(c["gateup_bytes"] / gu_t * 1e-9, 1),
+                    tflops=round(c["gateup_flop"] / gu_t * 1e-12, 2),
+                    bytes=c["gateup_bytes"], flop=c["gateup_flop"]),
+        routing=dict(experts_used=U,
+                     hot16_share=round(float(np.sort(hist)[::-1][:16].sum() / hist.sum()), 4),
+                     tokens_per_expert=dict(min=int(hist.min()), median=float(np.median(hist)),
+                                            max=int(hist.max()))),
     )
-    del ws
-    return out, ids_h
 
 
-def measure_single_launch(wl, moe, synth, copies, steps, warmup, ms_multi):
+def run_workload(wl, moe, synth, copies, warmup, steps, use_bias=True, sample=64):
+    """Time one workload and keep what the CPU leg compares: all ids and the
+    outputs of an evenly spaced sample of tokens."""
+    import numpy as np
+    L = Layer(wl, moe, synth, copies, use_bias)
+    ms = time_steps(L.step, warmup, steps)
+    stage = L.stage_ms(5)
+    ids_h = L.ids.cpu().numpy()
+    toks = np.unique(np.linspace(0, wl.T - 1, min(wl.T, sample)).round().astype(np.int64))
+    y_s = L.y[toks].float().cpu().numpy()
+    rec = summarize(wl, ms, stage, ids_h)
+    keep = dict(wl=wl, x=L.x_host, rw=L.rw_host, rb=L.rb_host, ids=ids_h, toks=toks, y=y_s)
+    L.free()
+    return rec, keep
+
+
+def measure_single_launch(wl, moe, synth, copies, warmup, steps, ms_multi):
     """moe_forward_fused (the whole layer in one launch) on the same inputs and
     weight copies as the multi-launch measurement; its output is checked equal,
     bit for bit, to moe_forward's on the first copy."""
-    import numpy as np
     import torch
-
-    def dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(a).cuda()
-
-    x = dev(synth.gen_x(wl))
-    rw_h, rb_h, _ = synth.gen_router(wl)
-    rw, rb = dev(rw_h), (dev(rb_h) if wl.use_bias else None)
-    cfg = moe.make_config(wl.T, wl.H, wl.E, wl.k, wl.I, wl.Is, wl.routed_scaling,
-                          wl.renormalize, wl.limit, wl.limit_shared)
-    ws = moe.alloc_workspace(cfg)
-    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
-    y_ref = torch.empty_like(y)
-    moe.moe_forward(cfg, x, rw, rb, *copies[0], y_ref, None, None, ws)
-    moe.moe_forward_fused(cfg, x, rw, rb, *copies[0], y, None, None, ws)
+    L = Layer(wl, moe, synth, copies)
+    y_ref = torch.empty_like(L.y)
+    moe.moe_forward(L.cfg, L.x, L.rw, L.rb, *copies[0], y_ref, None, None, L.ws)
+    moe.moe_forward_fused(L.cfg, L.x, L.rw, L.rb, *copies[0], L.y, None, None, L.ws)
     torch.cuda.synchronize()
-    identical = bool(torch.equal(y.view(torch.int16), y_ref.view(torch.int16)))
-    for i in range(warmup):
-        moe.moe_forward_fused(cfg, x, rw, rb, *copies[i % len(copies)], y, None, None, ws)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        moe.moe_forward_fused(cfg, x, rw, rb, *copies[i % len(copies)], y, None, None, ws)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    del ws
-    return dict(ms_per_step=round(ms, 5), tokens_per_s=round(wl.T / (ms * 1e-3), 1),
-                vs_multi_launch=round(ms_multi / ms, 3), identical_to_multi_launch=identical)
+    identical = bool(torch.equal(L.y.view(torch.int16), y_ref.view(torch.int16)))
+
+    def step(i):
+        moe.moe_forward_fused(L.cfg, L.x, L.rw, L.rb, *copies[i % len(copies)], L.y, None, None,
+                              L.ws)
+
+    ms = time_steps(step, warmup, steps)
+    med = _pct(ms, 50)
+    L.free()
+    return dict(ms=dict(median=round(med, 5), p10=round(_pct(ms, 10), 5),
+                        p90=round(_pct(ms, 90), 5)),
+                tokens_per_s=round(wl.T / (med * 1e-3), 1),
+                vs_multi_launch=round(ms_multi / med, 3), identical_to_multi_launch=identical)
 
 
-def measure_fp8(wl, moe, synth, copies8, shared, steps, warmup):
+def measure_fp8(wl, moe, synth, copies8, shared, warmup, steps):
     """moe_forward_fp8 (routed experts as e4m3 codes + row scales) on the
     workload's inputs, the copies of the FP8 weights rotated per step."""
     import numpy as np
-    import torch
-
-    def dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(a).cuda()
-
-    x = dev(synth.gen_x(wl))
-    rw_h, rb_h, _ = synth.gen_router(wl)
-    rw, rb = dev(rw_h), (dev(rb_h) if wl.use_bias else None)
-    cfg = moe.make_config(wl.T, wl.H, wl.E, wl.k, wl.I, wl.Is, wl.routed_scaling,
-                          wl.renormalize, wl.limit, wl.limit_shared)
-    ws = moe.alloc_workspace(cfg)
-    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
-    ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
-    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+    L = Layer(wl, moe, synth, [()])
 
     def step(i):
-        moe.moe_forward_fp8(cfg, x, rw, rb, *copies8[i % len(copies8)], *shared, y, ids, w, ws)
+        moe.moe_forward_fp8(L.cfg, L.x, L.rw, L.rb, *copies8[i % len(copies8)], *shared, L.y,
+                            L.ids, L.w, L.ws)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    U = int(np.count_nonzero(np.bincount(ids.cpu().numpy().ravel(), minlength=wl.E)))
+    ms = time_steps(step, warmup, steps)
+    med = _pct(ms, 50)
+    U = int(np.count_nonzero(np.bincount(L.ids.cpu().numpy().ravel(), minlength=wl.E)))
     H, I, Is, T, E, P = wl.H, wl.I, wl.Is, wl.T, wl.E, wl.P
     nbytes = U * (3.0 * H * I + 4.0 * (2 * I + H)) + 3.0 * H * Is * 2 + E * H * 4 + T * H * 2 * 2
     flop = 2.0 * T * H * E + 6.0 * P * H * I + 6.0 * T * H * Is
-    t = ms * 1e-3
-    return dict(ms_per_step=round(ms, 5), tokens_per_s=round(T / t, 1),
+    t = med * 1e-3
+    L.free()
+    return dict(ms=dict(median=round(med, 5), p10=round(_pct(ms, 10), 5),
+                        p90=round(_pct(ms, 90), 5)),
+                tokens_per_s=round(T / t, 1),
                 gbs=round(nbytes / t * 1e-9, 1), frac_hbm=round(nbytes / t * 1e-9 / HBM_PEAK_GBS, 4),
                 tflops=round(flop / t * 1e-12, 2),
                 frac_mfma=round(flop / t * 1e-12 / BF16_PEAK_TFLOPS, 4), experts_used=U,
                 algorithmic_bytes=nbytes)
 
 
-def measure_dense(wl, moe, synth, steps, warmup):
+def measure_dense(wl, moe, synth, warmup, steps):
     """The dense SwiGLU FFN (moe_dense_forward) on its workload: ms/step and
     the MFMA rate of its 6*T*H*I FLOPs."""
-    import numpy as np
     import torch
-
-    def dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-
     inp = synth.make_inputs(wl)
-    x, wg, wu, wd = dev(inp.x), dev(inp.ws_gate), dev(inp.ws_up), dev(inp.ws_down)
+    x, wg, wu, wd = _dev(inp.x), _dev(inp.ws_gate), _dev(inp.ws_up), _dev(inp.ws_down)
     cfg = moe.make_dense_config(wl.T, wl.H, wl.Is, wl.limit_shared)
     ws = moe.alloc_dense_workspace(cfg)
     y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
-    for _ in range(warmup):
-        moe.moe_dense_forward(cfg, x, wg, wu, wd, y, ws)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        moe.moe_dense_forward(cfg, x, wg, wu, wd, y, ws)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = time_steps(lambda i: moe.moe_dense_forward(cfg, x, wg, wu, wd, y, ws), warmup, steps)
+    med = _pct(ms, 50)
     flop = 6.0 * wl.T * wl.H * wl.Is
-    tf = flop / (ms * 1e-3) * 1e-12
-    return dict(tokens=wl.T, hidden=wl.H, inter=wl.Is, ms_per_step=round(ms, 5),
-                tokens_per_s=round(wl.T / (ms * 1e-3), 1), tflops=round(tf, 2),
+    tf = flop / (med * 1e-3) * 1e-12
+    return dict(tokens=wl.T, hidden=wl.H, inter=wl.Is,
+                ms=dict(median=round(med, 5), p10=round(_pct(ms, 10), 5),
+                        p90=round(_pct(ms, 90), 5)),
+                tokens_per_s=round(wl.T / (med * 1e-3), 1), tflops=round(tf, 2),
                 frac_mfma=round(tf / BF16_PEAK_TFLOPS, 4))
 
 
-def roofline(wl, res, bound):
-    g = res["gateup"]
-    if bound == "hbm":
-        tr = traffic_for("gateup_kernel", wl.name)
-        return dict(kernel="gateup_kernel", bound="hbm", achieved=round(g["gbs"], 1),
-                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(g["gbs"] / HBM_PEAK_GBS, 4),
-                    traffic=tr, algorithmic_bytes_per_launch=g["bytes"],
-                    avg_launch_ms=round(g["ms"], 5))
+def roofline(wl, rec, bound):
+    """Roofline of the workload's dominant kernel, gate/up: algorithmic bytes
+    (decode) or FLOPs (prefill) per launch over its event-timed mean launch."""
+    g = rec["gateup"]
     tr = traffic_for("gateup_kernel", wl.name)
-    return dict(kernel="gateup_kernel", bound="mfma", achieved=round(g["tflops"], 1),
-                peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(g["tflops"] / BF16_PEAK_TFLOPS, 4),
-                traffic=tr, algorithmic_flop_per_launch=g["flop"], avg_launch_ms=round(g["ms"], 5))
+    if bound == "hbm":
+        return dict(kernel="gateup_kernel", bound="hbm", achieved=g["gbs"], peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(g["gbs"] / HBM_PEAK_GBS, 4), traffic=tr,
+                    algorithmic_bytes_per_launch=g["bytes"], avg_launch_ms=g["ms"])
+    return dict(kernel="gateup_kernel", bound="mfma", achieved=g["tflops"], peak=BF16_PEAK_TFLOPS,
+                unit="TFLOP/s", frac=round(g["tflops"] / BF16_PEAK_TFLOPS, 4), traffic=tr,
+                algorithmic_flop_per_launch=g["flop"], avg_launch_ms=g["ms"])
 
 
-def cpu_baseline(wl, inp):
-    """The oracle on the whole decode batch, repeated until at least 10 s of
-    CPU time have passed (capped at 30 s)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(head, keeps, experts_host, synth):
+    """The oracle (double precision, one thread per token range) on the host:
+    the headline workload's whole batch repeated for at least 10 s, then a
+    bounded sample of every timed workload, whose outputs are compared with
+    the GPU's outputs for the same tokens."""
+    import numpy as np
     import oracle
     threads = oracle.default_threads()
+    info = dict(cores=threads, host_hardware_threads=oracle.hardware_threads(),
+                affinity_cpus=len(os.sched_getaffinity(0)), cpu_model=cpu_model())
+
+    def inputs(k):
+        wl = k["wl"]
+        ex = experts_host if wl.name != "tiny" else synth.gen_experts(wl)
+        return synth.Inputs(wl, k["x"], k["rw"], k["rb"], *ex)
+
+    hk = keeps[head]
+    wl = hk["wl"]
+    inp = inputs(hk)
     cfg = oracle.cfg_of(wl)
-    reps, t0 = 0, time.perf_counter()
+    walls, t0 = [], time.perf_counter()
     while True:
+        a = time.perf_counter()
         oracle.forward(cfg, inp, threads=threads)
-        reps += 1
+        walls.append(time.perf_counter() - a)
         dt = time.perf_counter() - t0
-        if dt >= 10.0 or dt * (reps + 1) / reps > 30.0:
+        if dt >= 10.0 or dt * (len(walls) + 1) / len(walls) > 30.0:
             break
-    return dict(value=round(reps * wl.T / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{reps} passes over all {wl.T} tokens of the {wl.name} workload "
-                       f"(double-precision per-token oracle, {dt:.1f} s wall)")
+    med = float(np.median(walls))
+    out = dict(value=round(wl.T / med, 3), unit="tokens/s", kind="oracle", **info,
+               sample=f"median of {len(walls)} passes over all {wl.T} tokens of the {wl.name} "
+                      f"workload (double-precision per-token oracle, {dt:.1f} s wall)")
+    per = {}
+    for name, k in keeps.items():
+        wl = k["wl"]
+        inp = inputs(k)
+        cfg = oracle.cfg_of(wl)
+        a = time.perf_counter()
+        ref = oracle.route(cfg, inp.x, inp.router_w, inp.router_b, threads=threads)
+        t_route = time.perf_counter() - a
+        a = time.perf_counter()
+        yr = oracle.forward(cfg, inp, tokens=k["toks"], threads=threads)
+        t_fwd = time.perf_counter() - a
+        same = np.all(np.sort(yr["ids"], 1) == np.sort(k["ids"][k["toks"]], 1), 1)
+        M = float(np.max(np.abs(yr["y"][same]))) if same.any() else 0.0
+        err = float(np.max(np.abs(k["y"][same] - yr["y"][same]))) if same.any() else 0.0
+        per[name] = dict(
+            oracle_tokens_per_s=round(len(k["toks"]) / t_fwd, 2), sample_tokens=len(k["toks"]),
+            oracle_wall_s=round(t_fwd, 3), route_all_tokens_s=round(t_route, 3),
+            near_tie_tokens=int(np.count_nonzero((ref["gap"] > 0) & (ref["gap"] < 1e-5))),
+            ids_equal_tokens=int(np.count_nonzero(np.all(np.sort(ref["ids"], 1) ==
+                                                         np.sort(k["ids"], 1), 1))),
+            sample_max_abs_err=err, sample_err_over_M=round(err / M, 6) if M else 0.0,
+            sample_pass=bool(err <= 1e-2 * M + 1e-3))
+        log(f"[bench] oracle {name}: {per[name]}")
+    out["per_config"] = per
+    return out
 
 
 def main():
@@ -453,106 +620,125 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.load_library()
-    wl = synth.WORKLOADS[args.config]
-    log(f"[bench] generating inputs for {wl.name} (T={wl.T})")
+    head = args.config
+    wl = synth.WORKLOADS[head]
+    log(f"[bench] generating expert weights for {wl.name} (H {wl.H}, E {wl.E}, I {wl.I})")
     experts_host = synth.gen_experts(wl)
-
-    def dev(a):
-        a = np.ascontiguousarray(a)
-        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-
-    base = [dev(a) for a in experts_host]
+    base = [_dev(a) for a in experts_host]
     ncopy = max(1, args.weight_copies if wl.name != "tiny" else 1)
     copies = [tuple(base)]
     for _ in range(ncopy - 1):
         copies.append(tuple(t.clone() for t in base))
     torch.cuda.synchronize()
-    log(f"[bench] {ncopy} weight copies resident; timing {args.steps} steps")
-    res, _ = measure(wl, moe, synth, experts_host, copies, args.steps, args.warmup)
-    log(f"[bench] {wl.name}: {res['ms_per_step']:.4f} ms/step, stages {res['stage_ms']}")
+    log(f"[bench] {ncopy} weight copies resident; timing {args.steps} steps of {wl.name}")
 
-    bound = "hbm" if wl.name in ("decode", "tiny") else "mfma"
-    rec = dict(metric=METRIC, value=round(res["tokens_per_s"], 1), unit="tokens/s", n_gpus=1,
-               steps=args.steps, warmup=args.warmup, ms_per_step=round(res["ms_per_step"], 5),
+    # The headline: exactly `steps` steps after `warmup`, bracketed by device
+    # synchronisations, wall clock.
+    L = Layer(wl, moe, synth, copies)
+    for i in range(args.warmup):
+        L.step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        L.step(i)
+    torch.cuda.synchronize()
+    ms_head = (time.perf_counter() - t0) * 1e3 / args.steps
+    L.free()
+    del L
+    log(f"[bench] {wl.name}: {ms_head:.4f} ms/step")
+
+    # Every timed workload: fixed warm-up and step counts, per-step events.
+    plan = [(head, True)]
+    if not args.only_headline:
+        full = ["decode", "prefill", "skewed", "long"]
+        plan = [("tiny", True)] + [(n, True) for n in full] + \
+               [("decode", False), ("prefill", False)]
+        if head not in full + ["tiny"]:
+            plan.insert(0, (head, True))
+    configs, supplements, keeps = {}, {}, {}
+    for name, use_bias in plan:
+        cwl = synth.WORKLOADS[name]
+        if name == "tiny":
+            cc = [tuple(_dev(a) for a in synth.gen_experts(cwl))]
+        else:
+            cc = copies if name == "decode" else copies[:2]
+        steps = 100 if name in ("tiny", "decode") else 20
+        label = name if use_bias else f"{name}_no_bias"
+        log(f"[bench] {label}: T={cwl.T}, 5 warm-up + {steps} timed steps")
+        rec, keep = run_workload(cwl, moe, synth, cc, 5, steps, use_bias)
+        rec["weight_copies"] = len(cc)
+        log(f"[bench] {label}: median {rec['ms']['median']:.4f} ms, U={rec['routing']['experts_used']}, "
+            f"stages {rec['stage_ms']}")
+        if use_bias:
+            configs[name] = rec
+        else:
+            rec["note"] = ("supplement: the same workload with router bias 0 (near-uniform "
+                           "routing, as the workload prose describes); never replaces the row above")
+            supplements[label] = rec
+        keeps[label] = keep
+        torch.cuda.empty_cache()
+
+    hrec = configs.get(head)
+    bound = "hbm" if head in ("decode", "tiny") else "mfma"
+    rec = dict(metric=METRIC, value=round(wl.T / (ms_head * 1e-3), 1), unit="tokens/s", n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=round(ms_head, 5),
                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
                data="synthetic",
                config=dict(workload=wl.name, tokens=wl.T, hidden=wl.H, experts=wl.E, top_k=wl.k,
                            inter=wl.I, inter_shared=wl.Is, swiglu_limit=wl.limit,
                            weight_copies=ncopy, seed=wl.seed, parallelism="single GPU"),
-               roofline=roofline(wl, res, bound),
-               layer=dict(tflops=round(res["tflops"], 2), gbs=round(res["gbs"], 1),
-                          frac_mfma=round(res["frac_mfma"], 4), frac_hbm=round(res["frac_hbm"], 4),
-                          stage_ms=res["stage_ms"], experts_used=res["experts_used"],
-                          tokens_per_expert=res["tokens_per_expert"],
-                          hot16_share=round(res["hot16_share"], 3)),
-               note=NOTE)
+               roofline=roofline(wl, hrec, bound) if hrec else None,
+               configs=configs, supplements=supplements, note=NOTE)
+    if "prefill" in configs:
+        rec["prefill"] = dict(tokens_per_s=configs["prefill"]["tokens_per_s"],
+                              ms=configs["prefill"]["ms"],
+                              frac_mfma=configs["prefill"]["frac_mfma"],
+                              roofline=roofline(synth.WORKLOADS["prefill"], configs["prefill"],
+                                                "mfma"))
 
-    if wl.name == "decode" and not args.no_secondary:
-        pw = synth.WORKLOADS["prefill"]
-        log("[bench] prefill T=8192")
-        pres, _ = measure(pw, moe, synth, experts_host, copies[:2], max(5, args.steps // 5),
-                          max(2, args.warmup // 2))
-        rec["prefill"] = dict(tokens_per_s=round(pres["tokens_per_s"], 1),
-                              ms_per_step=round(pres["ms_per_step"], 5),
-                              tflops=round(pres["tflops"], 2),
-                              frac_mfma=round(pres["frac_mfma"], 4),
-                              roofline=roofline(pw, pres, "mfma"), stage_ms=pres["stage_ms"],
-                              experts_used=pres["experts_used"])
-        log(f"[bench] prefill: {pres['ms_per_step']:.4f} ms/step, stages {pres['stage_ms']}")
-
-    if wl.name == "decode" and not args.no_secondary and not args.no_extra:
-        # Second workloads on the same kernels: the predecessor Step-3's MoE shape and the
-        # dense SwiGLU FFN of the first layers.
+    if head == "decode" and not args.only_headline and not args.no_extra:
+        # Second workloads on the same kernels.
         rec["workloads"] = {}
-        # The same decode step in one launch (moe_forward_fused)
         rec["workloads"]["decode_single_launch"] = measure_single_launch(
-            wl, moe, synth, copies, args.steps, args.warmup, res["ms_per_step"])
-        log(f"[bench] decode single launch: "
-            f"{rec['workloads']['decode_single_launch']['ms_per_step']:.4f} ms/step")
+            wl, moe, synth, copies, 5, 100, configs["decode"]["ms"]["median"])
+        log(f"[bench] decode single launch: {rec['workloads']['decode_single_launch']}")
         sw = synth.WORKLOADS["step3"]
         log(f"[bench] step3 T={sw.T} (H {sw.H}, E {sw.E}, k {sw.k}, I {sw.I})")
         s_host = synth.gen_experts(sw)
-        s_dev = [tuple(dev(a) for a in s_host)]
+        s_dev = [tuple(_dev(a) for a in s_host)]
         del s_host
-        sres, _ = measure(sw, moe, synth, None, s_dev, 10, 3)
+        srec, _ = run_workload(sw, moe, synth, s_dev, 3, 10)
         rec["workloads"]["step3"] = dict(
             tokens=sw.T, hidden=sw.H, experts=sw.E, top_k=sw.k, inter=sw.I, inter_shared=sw.Is,
-            ms_per_step=round(sres["ms_per_step"], 5), tokens_per_s=round(sres["tokens_per_s"], 1),
-            tflops=round(sres["tflops"], 2), frac_mfma=round(sres["frac_mfma"], 4),
-            experts_used=sres["experts_used"], stage_ms=sres["stage_ms"])
-        log(f"[bench] step3: {sres['ms_per_step']:.4f} ms/step")
+            ms=srec["ms"], tokens_per_s=srec["tokens_per_s"], tflops=srec["tflops"],
+            frac_mfma=srec["frac_mfma"], experts_used=srec["routing"]["experts_used"],
+            stage_ms=srec["stage_ms"])
+        log(f"[bench] step3: {srec['ms']}")
         del s_dev
         torch.cuda.empty_cache()
-        # FP8 (e4m3) routed-expert weights on the decode and prefill workloads
         log("[bench] fp8 experts: decode and prefill")
         f8 = synth.gen_experts_fp8(wl)
-
-        def dev8(a):
-            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-        c8 = [tuple(dev8(a) for a in (f8.w8_gate, f8.w8_up, f8.w8_down, f8.s_gate, f8.s_up,
+        c8 = [tuple(_dev(a) for a in (f8.w8_gate, f8.w8_up, f8.w8_down, f8.s_gate, f8.s_up,
                                       f8.s_down))]
         for _ in range(ncopy - 1):
             c8.append(tuple(t.clone() for t in c8[0]))
         del f8
         shared = tuple(copies[0][3:6])
-        rec["workloads"]["decode_fp8"] = measure_fp8(wl, moe, synth, c8, shared, args.steps,
-                                                     args.warmup)
-        log(f"[bench] decode fp8: {rec['workloads']['decode_fp8']['ms_per_step']:.4f} ms/step")
+        rec["workloads"]["decode_fp8"] = measure_fp8(wl, moe, synth, c8, shared, 5, 100)
+        log(f"[bench] decode fp8: {rec['workloads']['decode_fp8']}")
         rec["workloads"]["prefill_fp8"] = measure_fp8(synth.WORKLOADS["prefill"], moe, synth,
-                                                      c8[:2], shared, 10, 3)
-        log(f"[bench] prefill fp8: {rec['workloads']['prefill_fp8']['ms_per_step']:.4f} ms/step")
+                                                      c8[:2], shared, 5, 20)
+        log(f"[bench] prefill fp8: {rec['workloads']['prefill_fp8']}")
         del c8
         torch.cuda.empty_cache()
         dw = synth.WORKLOADS["dense"]
         log(f"[bench] dense FFN T={dw.T} I={dw.Is}")
-        rec["workloads"]["dense_ffn"] = measure_dense(dw, moe, synth, 10, 3)
-        log(f"[bench] dense: {rec['workloads']['dense_ffn']['ms_per_step']:.4f} ms/step")
+        rec["workloads"]["dense_ffn"] = measure_dense(dw, moe, synth, 3, 10)
+        log(f"[bench] dense: {rec['workloads']['dense_ffn']}")
 
-    if not args.no_cpu and wl.name in ("decode", "tiny"):
+    if not args.no_cpu and head in keeps:
         log("[bench] CPU oracle baseline")
-        inp = synth.make_inputs(wl, experts=experts_host)
-        rec["cpu_baseline"] = cpu_baseline(wl, inp)
+        rec["cpu_baseline"] = cpu_baseline(head, keeps, experts_host, synth)
     gp = torch.cuda.get_device_properties(0)
     rec["device"] = dict(name=gp.name, arch=getattr(gp, "gcnArchName", ""),
                          compute_units=gp.multi_processor_count)
