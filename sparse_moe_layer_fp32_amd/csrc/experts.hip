@@ -8,9 +8,14 @@ namespace moe {
 
 namespace {
 
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0, int AV = 0>
+// One unit (row tile, column tile) per block.  With e4m3 routed weights
+// (WF = 1) the shared expert's bf16 tiles in the same launch take their own
+// k step BK0 and ring depth S0, so that both bodies fit the LDS.
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0, int AV = 0,
+          int BK0 = BK, int S0 = S>
 __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
-  using C0 = Cfg<BM, BN, BK, WM, WN, S, 0, AV>;
+  static_assert(WF == 1 || (BK0 == BK && S0 == S), "one body without e4m3 weights");
+  using C0 = Cfg<BM, BN, BK0, WM, WN, S0, 0, AV>;
   using C1 = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
   constexpr int LDS = C0::LDS_BYTES > C1::LDS_BYTES ? C0::LDS_BYTES : C1::LDS_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
@@ -31,7 +36,7 @@ __global__ __launch_bounds__(64 * WM * WN) void expert_gemm(ExpertArgs a) {
   }
   if constexpr (WF == 1) {
     if (e == a.E) {  // shared expert: bf16 weights
-      gemm_tile<MODE, BM, BN, BK, WM, WN, S, 0, AV>(a, smem, tc, e, row0);
+      gemm_tile<MODE, BM, BN, BK0, WM, WN, S0, 0, AV>(a, smem, tc, e, row0);
       return;
     }
   }
@@ -142,7 +147,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                   static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
 }
 
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0, int AV = 0>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WF = 0, int AV = 0,
+          int BK0 = BK, int S0 = S>
 hipError_t launch_one(const ExpertArgs& a, int tile_capacity, int NT, hipStream_t stream) {
   using C = Cfg<BM, BN, BK, WM, WN, S, WF, AV>;
   const int64_t units = static_cast<int64_t>(tile_capacity) * NT;
@@ -150,7 +156,7 @@ hipError_t launch_one(const ExpertArgs& a, int tile_capacity, int NT, hipStream_
   if (grid <= 0) return hipSuccess;
   ExpertArgs b = a;
   b.NT = NT;
-  expert_gemm<MODE, BM, BN, BK, WM, WN, S, WF, AV>
+  expert_gemm<MODE, BM, BN, BK, WM, WN, S, WF, AV, BK0, S0>
       <<<static_cast<unsigned>(grid), C::THREADS, 0, stream>>>(b);
   return hipGetLastError();
 }
@@ -202,10 +208,11 @@ int experts_tile_capacity(int64_t T, int P, int E, int with_shared, int shape) {
 // ring when I and Is are multiples of 128 (else 64 h columns, k step 128, 4
 // waves, 3-deep: every weight row read in 256-byte pieces); down 256 output
 // columns, k step 64, 8 waves, 3-deep (128 columns and 4 waves when H is not
-// a multiple of 256).  The e4m3 kernels: 64 x 256 tiles, k step 64, 4-deep
-// ring, 8 waves (their k steps carry half the bytes of a bf16 step; the
-// shared expert's bf16 tiles in them take the whole 160 KB of LDS), else
-// 64 x 128 with a 3-deep ring.
+// a multiple of 256).  The e4m3 kernels: 64 x 256 tiles, 8 waves, k step 128
+// with a 3-deep ring (each weight row piece a whole 128-byte line, which
+// takes the non-temporal hint; FP8 decode -11% against k step 64), the
+// shared expert's bf16 tiles in them at k step 64 with a 4-deep ring (the
+// whole 160 KB of LDS); else 64 x 128 at k step 64 with a 3-deep ring.
 hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipStream_t stream,
                          int fp8) {
   const int maxn = std::max(a.I, a.Is);
@@ -214,7 +221,8 @@ hipError_t launch_gateup(const ExpertArgs& a, int shape, int tile_capacity, hipS
       return launch_persistent<0, 256, 256, 64, 2, 4, 3, 1, 1>(a, (maxn + 127) / 128, a.queue,
                                                                stream);
     if (a.I % 128 == 0 && a.Is % 128 == 0)
-      return launch_one<0, 64, 256, 64, 2, 4, 4, 1>(a, tile_capacity, maxn / 128, stream);
+      return launch_one<0, 64, 256, 128, 2, 4, 3, 1, 0, 64, 4>(a, tile_capacity, maxn / 128,
+                                                              stream);
     return launch_one<0, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, (maxn + 63) / 64, stream);
   }
   if (shape == kTileBig)
@@ -231,6 +239,9 @@ hipError_t launch_down(const ExpertArgs& a, int shape, int tile_capacity, hipStr
     if (shape == kTileBig)
       return launch_persistent<1, 256, 256, 64, 2, 4, 3, 1, 1>(a, a.H / 256, a.queue + kNumXcd,
                                                                stream);
+    if (a.H % 256 == 0 && a.I % 128 == 0 && a.Is % 128 == 0)
+      return launch_one<1, 64, 256, 128, 2, 4, 3, 1, 0, 64, 4>(a, tile_capacity, a.H / 256,
+                                                              stream);
     if (a.H % 256 == 0)
       return launch_one<1, 64, 256, 64, 2, 4, 4, 1>(a, tile_capacity, a.H / 256, stream);
     return launch_one<1, 64, 128, 64, 2, 2, 3, 1>(a, tile_capacity, a.H / 128, stream);
