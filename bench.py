@@ -82,6 +82,8 @@ _SHORT = {"decode": "--config decode --steps 4 --warmup 1",
           "skewed": "--config skewed --steps 2 --warmup 1 --weight-copies 1",
           "long": "--config long --steps 2 --warmup 1 --weight-copies 1"}
 MFMA_COUNTERS = "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE"
+STALL_COUNTERS = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_LDS_IDX_ACTIVE "
+                  "SQ_LDS_BANK_CONFLICT SQ_LDS_DATA_FIFO_FULL SQ_BUSY_CYCLES")
 PROFILE_COMMANDS = {}
 for _w in _RUNS:
     PROFILE_COMMANDS[f"kt_{_w}"] = (
@@ -91,6 +93,9 @@ for _w in ("prefill", "skewed", "long"):
     PROFILE_COMMANDS[f"pmc_mfma_{_w}"] = (
         f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv "
         f"-d DIR/pmc_mfma_{_w} -o run -- {_B} {_SHORT[_w]}")
+    PROFILE_COMMANDS[f"pmc_stall_{_w}"] = (
+        f"rocprofv3 --pmc {STALL_COUNTERS} --output-format csv -d DIR/pmc_stall_{_w} -o run -- "
+        f"{_B} {_SHORT[_w]}")
     PROFILE_COMMANDS[f"pmc_l2_{_w}"] = (
         f"rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d DIR/pmc_l2_{_w} -o run "
         f"-- {_B} {_SHORT[_w]}")
@@ -207,6 +212,42 @@ def summarize_profiles(d):
         with open(os.path.join(out_dir, f"mfma_{wl}.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
         wrote.append(f"mfma_{wl}.md")
+
+    st = [wl for wl in ("prefill", "skewed", "long") if have(f"pmc_stall_{wl}")]
+    if st:
+        lines = ["# Where the waves' time goes (rocprofv3 SQ counters)", "",
+                 "Commands (run from the repository root with TMPDIR=/tmp; DIR = an output "
+                 "directory):", "", "```"]
+        lines += [PROFILE_COMMANDS[f"pmc_stall_{wl}"] for wl in st]
+        lines += ["```", "",
+                  "SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY and SQ_WAIT_INST_LDS are "
+                  "wave-cycles summed over the waves (quad-cycle units, so their ratios are "
+                  "exact): *waiting* is the share of a wave's life spent in s_waitcnt or at a "
+                  "barrier, *issue-blocked* the share it had an instruction ready that could not "
+                  "issue, *LDS-issue* the part of that blocked on the LDS.  SQ_LDS_IDX_ACTIVE and "
+                  "SQ_LDS_BANK_CONFLICT are LDS cycles summed over the CUs of each shader engine; "
+                  "*LDS busy* divides them by SQ_BUSY_CYCLES times 32 CUs per engine.", "",
+                  "| Workload | Kernel | Waiting | Issue-blocked | LDS-issue | LDS busy | "
+                  "Bank-conflict cycles / LDS cycles | LDS data FIFO full cycles |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for wl in st:
+            cs = counters(f"pmc_stall_{wl}")
+            for k in sorted(cs, key=lambda k: -cs[k].get("SQ_WAVE_CYCLES", 0)):
+                if "moe::" not in k:
+                    continue
+                c = cs[k]
+                wc = c.get("SQ_WAVE_CYCLES", 0.0) or float("nan")
+                busy = c.get("SQ_BUSY_CYCLES", 0.0) or float("nan")
+                lds = c.get("SQ_LDS_IDX_ACTIVE", 0.0)
+                lines.append(
+                    f"| {wl} | `{_short(k)}` | {c.get('SQ_WAIT_ANY', 0) / wc:.3f} | "
+                    f"{c.get('SQ_WAIT_INST_ANY', 0) / wc:.3f} | {c.get('SQ_WAIT_INST_LDS', 0) / wc:.3f} | "
+                    f"{lds / (busy * 32):.3f} | "
+                    f"{c.get('SQ_LDS_BANK_CONFLICT', 0) / lds if lds else 0:.4f} | "
+                    f"{c.get('SQ_LDS_DATA_FIFO_FULL', 0):.3e} |")
+        with open(os.path.join(out_dir, "stalls.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        wrote.append("stalls.md")
 
     l2 = [wl for wl in ("prefill", "skewed", "long") if have(f"pmc_l2_{wl}")]
     if l2:
