@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--weight-copies", type=int, default=4)
     ap.add_argument("--only-headline", action="store_true",
                     help="time the --config workload only (no other workloads or supplements)")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="time only moe_forward_fp8 (e4m3 routed experts) on the --config "
+                         "workload, --steps after --warmup, and print its record (profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the second workloads (single launch, Step-3 MoE shape, FP8, "
@@ -104,6 +107,13 @@ for _w in ("decode", "prefill", "skewed", "long"):
         _k = f"pmc_{_c.split('_')[0].lower()}_{_w}"
         PROFILE_COMMANDS[_k] = (f"rocprofv3 --pmc {_c} --output-format csv -d DIR/{_k} -o run -- "
                                 f"{_B} {_SHORT[_w]}")
+PROFILE_COMMANDS["kt_decode_fp8"] = (
+    "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/kt_decode_fp8 -o run -- "
+    f"{_B} --fp8-only {_RUNS['decode']}")
+for _c in ("FETCH_SIZE", "WRITE_SIZE"):
+    _k = f"pmc_{_c.split('_')[0].lower()}_decode_fp8"
+    PROFILE_COMMANDS[_k] = (f"rocprofv3 --pmc {_c} --output-format csv -d DIR/{_k} -o run -- "
+                            f"{_B} --fp8-only {_SHORT['decode']}")
 for _c in ("FETCH_SIZE", "WRITE_SIZE"):
     _k = f"pmc_{_c.split('_')[0].lower()}_copy"
     PROFILE_COMMANDS[_k] = (f"rocprofv3 --pmc {_c} --output-format csv -d DIR/{_k} -o run -- "
@@ -150,7 +160,7 @@ def summarize_profiles(d):
     os.makedirs(out_dir, exist_ok=True)
     have = lambda k: os.path.isdir(os.path.join(d, k))  # noqa: E731
     wrote = []
-    for wl in _RUNS:
+    for wl in list(_RUNS) + ["decode_fp8"]:
         if not have(f"kt_{wl}"):
             continue
         rows = list(csv.DictReader(open(os.path.join(d, f"kt_{wl}", "run_kernel_stats.csv"))))
@@ -176,6 +186,15 @@ def summarize_profiles(d):
             agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
         return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
 
+    def gpu_info(name):
+        """(XCDs, CUs per shader engine) of the profiled GPU, from the run's agent info."""
+        path = os.path.join(d, name, "run_agent_info.csv")
+        if os.path.exists(path):
+            for r in csv.DictReader(open(path)):
+                if r.get("Name", "").startswith("gfx"):
+                    return int(r.get("Num_Xcc") or 1), int(r.get("Cu_Per_Engine") or 8)
+        return 8, 8
+
     def durations(name):
         """{kernel: mean duration in ns} from the kernel trace of the same run."""
         path = os.path.join(d, name, "run_kernel_trace.csv")
@@ -189,14 +208,16 @@ def summarize_profiles(d):
         if not have(f"pmc_mfma_{wl}"):
             continue
         cs, du = counters(f"pmc_mfma_{wl}"), durations(f"pmc_mfma_{wl}")
+        nxcc, _ = gpu_info(f"pmc_mfma_{wl}")
         lines = [f"# MFMA utilisation, {wl} workload (rocprofv3 counters)", "",
                  "Command (run from the repository root with TMPDIR=/tmp; DIR = an output directory):", "", "```",
                  PROFILE_COMMANDS[f"pmc_mfma_{wl}"], "```", "",
                  "MfmaUtil is rocprofv3's derived counter: the MFMA units' busy cycles summed "
                  "over the SIMDs, over the GPU's active cycles times the SIMD count.  Issued "
                  "bf16 MFMA work is SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP (padding rows "
-                 "included).  The clock is GRBM_GUI_ACTIVE over the kernel's duration in the "
-                 "same run.", "",
+                 "included).  The clock is GRBM_GUI_ACTIVE (summed over the GPU's "
+                 f"{nxcc} XCDs) over the number of XCDs and the kernel's duration in the same "
+                 "run; it is meaningful for kernels much longer than their launch.", "",
                  "| Kernel | MfmaUtil % | Issued bf16 TFLOP/launch | Duration us | Clock GHz | "
                  "Issued TFLOP/s |", "|---|---|---|---|---|---|"]
         for k in sorted(cs, key=lambda k: -cs[k].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0)):
@@ -205,7 +226,7 @@ def summarize_profiles(d):
             c = cs[k]
             fl = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
             dur = du.get(k)
-            clk = c.get("GRBM_GUI_ACTIVE", 0.0) / dur if dur else float("nan")
+            clk = c.get("GRBM_GUI_ACTIVE", 0.0) / nxcc / dur if dur else float("nan")
             rate = fl / (dur * 1e-9) * 1e-12 if dur else float("nan")
             lines.append(f"| `{_short(k)}` | {c.get('MfmaUtil', float('nan')):.1f} | {fl * 1e-12:.4f} | "
                          f"{dur / 1e3 if dur else float('nan'):.1f} | {clk:.3f} | {rate:.1f} |")
@@ -226,12 +247,14 @@ def summarize_profiles(d):
                   "barrier, *issue-blocked* the share it had an instruction ready that could not "
                   "issue, *LDS-issue* the part of that blocked on the LDS.  SQ_LDS_IDX_ACTIVE and "
                   "SQ_LDS_BANK_CONFLICT are LDS cycles summed over the CUs of each shader engine; "
-                  "*LDS busy* divides them by SQ_BUSY_CYCLES times 32 CUs per engine.", "",
+                  "*LDS busy* divides them by SQ_BUSY_CYCLES (summed over the engines) times the "
+                  "CUs per engine.", "",
                   "| Workload | Kernel | Waiting | Issue-blocked | LDS-issue | LDS busy | "
                   "Bank-conflict cycles / LDS cycles | LDS data FIFO full cycles |",
                   "|---|---|---|---|---|---|---|---|"]
         for wl in st:
             cs = counters(f"pmc_stall_{wl}")
+            _, cupe = gpu_info(f"pmc_stall_{wl}")
             for k in sorted(cs, key=lambda k: -cs[k].get("SQ_WAVE_CYCLES", 0)):
                 if "moe::" not in k:
                     continue
@@ -242,7 +265,7 @@ def summarize_profiles(d):
                 lines.append(
                     f"| {wl} | `{_short(k)}` | {c.get('SQ_WAIT_ANY', 0) / wc:.3f} | "
                     f"{c.get('SQ_WAIT_INST_ANY', 0) / wc:.3f} | {c.get('SQ_WAIT_INST_LDS', 0) / wc:.3f} | "
-                    f"{lds / (busy * 32):.3f} | "
+                    f"{lds / (busy * cupe):.3f} | "
                     f"{c.get('SQ_LDS_BANK_CONFLICT', 0) / lds if lds else 0:.4f} | "
                     f"{c.get('SQ_LDS_DATA_FIFO_FULL', 0):.3e} |")
         with open(os.path.join(out_dir, "stalls.md"), "w") as f:
@@ -277,7 +300,8 @@ def summarize_profiles(d):
         traffic = {"calibration": {"copy_bytes": cal_bytes, "fetch_kib": copy_fetch,
                                    "write_kib": copy_write, "fetch_factor": f_fetch,
                                    "write_factor": f_write}}
-        wls = [wl for wl in _RUNS if have(f"pmc_fetch_{wl}") and have(f"pmc_write_{wl}")]
+        wls = [wl for wl in list(_RUNS) + ["decode_fp8"]
+               if have(f"pmc_fetch_{wl}") and have(f"pmc_write_{wl}")]
         lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
                  "Each counter ran alone.  Scale: a plain 1 GiB device copy "
                  f"(`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = {copy_fetch:.0f} KiB and "
@@ -663,6 +687,18 @@ def main():
     moe.load_library()
     head = args.config
     wl = synth.WORKLOADS[head]
+    if args.fp8_only:
+        log(f"[bench] e4m3 expert weights for {wl.name}")
+        f8 = synth.gen_experts_fp8(wl)
+        c8 = [tuple(_dev(a) for a in (f8.w8_gate, f8.w8_up, f8.w8_down, f8.s_gate, f8.s_up,
+                                      f8.s_down))]
+        del f8
+        for _ in range(max(1, args.weight_copies) - 1):
+            c8.append(tuple(t.clone() for t in c8[0]))
+        shared = tuple(_dev(a) for a in synth.gen_experts(wl.with_(E=0, I=0))[3:])
+        rec = measure_fp8(wl, moe, synth, c8, shared, args.warmup, args.steps)
+        print(json.dumps(dict(workload=wl.name, routed_weights="e4m3", **rec)))
+        return
     log(f"[bench] generating expert weights for {wl.name} (H {wl.H}, E {wl.E}, I {wl.I})")
     experts_host = synth.gen_experts(wl)
     base = [_dev(a) for a in experts_host]
