@@ -1,6 +1,8 @@
 """The layer forward inside a captured HIP graph, and on a caller stream that
 is not the default one.  Every replay is checked bit for bit against the
 eager result, with eager work and synchronisations between replays."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -59,6 +61,39 @@ def test_forward_graph_replays(moe, name):
     for rep in range(3):
         y.fill_(0.0)
         other = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")
+        torch.cuda.synchronize()
+        gu.note(f"  replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.float().cpu().numpy(), y_ref), f"replay {rep} differs"
+        del other
+
+
+def test_noalloc_forward_graph_replays(moe):
+    """moe_forward_noalloc captured in a graph (its workspace is the library's
+    fixed scratch, so the capture holds no allocation): every replay equals
+    the eager moe_forward, bit for bit."""
+    import torch
+    wl = synth.WORKLOADS["tiny"].with_(name="noalloc_graph", **CASES["small"])
+    inp = synth.make_inputs(wl)
+    d = gu.upload(inp)
+    cfg = gu.cfg_of(wl)
+    args = (cfg, d.x, d.router_w, d.router_b, d.w_gate, d.w_up, d.w_down, d.ws_gate, d.ws_up,
+            d.ws_down)
+    y_ref = gu.run_forward(wl, d).y
+    s = torch.cuda.Stream()
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(s):  # the scratch address is looked up on this first call
+        moe.moe_forward_noalloc(*args, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.float().cpu().numpy(), y_ref)
+    gu.note("  capture moe_forward_noalloc")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_forward_noalloc(*args, y)
+    for rep in range(3):
+        y.fill_(0.0)
+        other = gu.run_forward(wl.with_(T=8), dataclasses.replace(d, x=d.x[:8]))
         torch.cuda.synchronize()
         gu.note(f"  replay {rep}")
         g.replay()
