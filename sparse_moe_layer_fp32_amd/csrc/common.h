@@ -77,13 +77,30 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // Blocks are dispatched to XCDs round-robin (block b -> XCD b % 8).  Given
 // `nvalid` units of work, give each XCD a contiguous range of units so that
 // blocks sharing operands share an L2.  Returns -1 for a block without work.
-__device__ __forceinline__ int xcd_remap(int bid, int nvalid) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int nvalid) {
   const int per = (nvalid + kNumXcd - 1) / kNumXcd;
   const int xcd = bid % kNumXcd;
   const int slot = bid / kNumXcd;
   if (slot >= per) return -1;
   const int u = xcd * per + slot;
   return u < nvalid ? u : -1;
+}
+
+// As xcd_remap, but the last `nlast` units (0 <= nlast <= nvalid) are dealt
+// over the XCDs one at a time and come first in each XCD's order, while the
+// others keep contiguous ranges: each XCD runs at most ceil(nlast / 8) of
+// them, all in its first round.  Needs ceil(nvalid / 8) + 1 blocks per XCD.
+__host__ __device__ __forceinline__ int xcd_remap_dealt(int bid, int nvalid, int nlast) {
+  const int nr = nvalid - nlast;
+  const int xcd = bid % kNumXcd;
+  const int slot = bid / kNumXcd;
+  const int mine = nlast / kNumXcd + (xcd < nlast % kNumXcd ? 1 : 0);
+  if (slot < mine) return nr + slot * kNumXcd + xcd;
+  const int per = (nr + kNumXcd - 1) / kNumXcd;
+  const int s = slot - mine;
+  if (s >= per) return -1;
+  const int u = xcd * per + s;
+  return u < nr ? u : -1;
 }
 
 __device__ __forceinline__ int mfma32_row(int r, int lane) {
