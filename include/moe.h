@@ -218,7 +218,9 @@ moe_status moe_forward_fused(const moe_config* cfg, const uint16_t* x, const flo
  * moe_workspace_size() exceeds it returns MOE_ERR_WORKSPACE before anything
  * is enqueued.  The call itself allocates nothing (no hipMalloc, hipFree or
  * allocating library routine); on its first call on a device it looks up
- * that device's scratch address.
+ * that device's scratch address.  The scratch used is the current HIP
+ * device's, so the stream must belong to the current device (as the buffers
+ * of every entry point do).
  * Every call on one GPU uses that GPU's one scratch array, which keeps the
  * last call's contents (each call writes what it reads first): calls that
  * overlap on one GPU -- on different streams or host threads without
