@@ -91,6 +91,10 @@ SMALL = {
     "big_tile_no_shared": dict(T=1500, H=768, E=6, k=3, I=384, Is=0, bias_var=0.2),
     # enough tokens for the wave-per-token top-k
     "many_tokens": dict(T=2500, H=256, E=40, k=6, I=64, Is=64, bias_var=0.2),
+    # the ABI's limits, E = 1024 and k = 32, on both top-k paths (a block per
+    # token below 2048 tokens, a wave per token from there)
+    "max_experts": dict(T=100, H=256, E=1024, k=32, I=64, Is=64, bias_var=0.2),
+    "max_experts_wave": dict(T=2100, H=256, E=1024, k=32, I=64, Is=64, bias_var=0.2),
 }
 
 
