@@ -95,6 +95,10 @@ SMALL = {
     # token below 2048 tokens, a wave per token from there)
     "max_experts": dict(T=100, H=256, E=1024, k=32, I=64, Is=64, bias_var=0.2),
     "max_experts_wave": dict(T=2100, H=256, E=1024, k=32, I=64, Is=64, bias_var=0.2),
+    # degenerate routing: one expert per token (every weight is the scaling
+    # factor), and a single expert that takes every token
+    "top1": dict(T=300, H=256, E=16, k=1, I=64, Is=64, bias_var=0.3),
+    "single_expert": dict(T=200, H=256, E=1, k=1, I=128, Is=0),
 }
 
 
