@@ -151,12 +151,13 @@ def _kernel_key(short):
     return base
 
 
-def summarize_profiles(d):
+def summarize_profiles(d, out_dir=None):
     """Turn the rocprofv3 CSV outputs under d (made by PROFILE_COMMANDS; any
-    subset) into the text summaries under profiles/ and profiles/traffic.json."""
+    subset) into the text summaries under out_dir (default profiles/) and its
+    traffic.json."""
     import csv
     import collections
-    out_dir = os.path.join(ROOT, "profiles")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
     have = lambda k: os.path.isdir(os.path.join(d, k))  # noqa: E731
     wrote = []
@@ -362,10 +363,10 @@ def counts(wl, U):
                 gateup_bytes=gu_bytes, gateup_flop=gu_flop)
 
 
-def traffic_for(kernel, workload):
+def traffic_for(kernel, workload, profiles_dir=None):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
