@@ -24,16 +24,18 @@
 //    the token gather of the gate/up GEMM costs nothing extra.  The 16-byte
 //    chunks of a row are XOR-swizzled so that the 64 lanes of a fragment
 //    read hit all 64 LDS banks once (no bank conflicts).
-//  * An S-stage ring: stages kt+1 .. kt+S-2 are in flight while stage kt is
-//    multiplied; per-wave `s_waitcnt vmcnt` plus a bare s_barrier order the
-//    ring (no full fence, which would drain the prefetches).
+//  * An S-stage ring (or a split ring, A and B in rings of their own: Cfg):
+//    stages kt+1 .. kt+S-2 are in flight while stage kt is multiplied;
+//    per-wave `s_waitcnt vmcnt` plus a bare s_barrier order the ring (no full
+//    fence, which would drain the prefetches).
 //  * Work comes from a device-side tile list (no host synchronisation); units
-//    are spread over the 8 XCDs in contiguous ranges and walked in groups of
-//    8 row tiles so that co-resident blocks share operands in their L2.
+//    are spread over the 8 XCDs in contiguous ranges (the big tiles: a queue
+//    per XCD, with stealing) and walked in groups of 8 row tiles so that
+//    co-resident blocks share operands in their L2.
 //
 // Two tile families: 256 x 256 (one block per CU, 8 waves of 128 x 64) for
-// many rows per expert, and 64-row tiles with a 3-deep ring for few rows per
-// expert, where the GEMMs stream weights at HBM rate.
+// many rows per expert, and 64-row tiles with 3- or 4-deep rings for few rows
+// per expert, where the GEMMs stream weights at HBM rate.
 
 #pragma once
 
