@@ -134,12 +134,21 @@ def _short(name):
     return name.split("(")[0].strip()
 
 
+def _code_only(text):
+    """C++ source without its comments, trailing blanks and empty lines (the
+    hashed sources hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def _src_sha(fnames):
-    """SHA-256 over the given kernel sources, in order."""
+    """SHA-256 over the code of the given kernel sources, in order: edits to
+    comments leave it, and counters taken on the same code, valid."""
     h = hashlib.sha256()
     for fname in fnames:
-        with open(os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", fname), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", fname)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -88,3 +88,11 @@ def test_traffic_lookup_follows_the_kernel_source(prof):
     t["gateup_kernel:decode"]["source_sha256"] = "0" * 64
     json.dump(t, open(path, "w"))
     assert bench.traffic_for("gateup_kernel", "decode", out) is None
+
+
+def test_source_hash_sees_code_not_comments():
+    src = "// header\nint f(int a) {  // the sum\n  /* two\n lines */ return a + 1;\n}\n"
+    assert bench._code_only(src) == bench._code_only(
+        "// another header\n\nint f(int a) {\n  return a + 1;  /* one */\n}\n")
+    assert bench._code_only(src) != bench._code_only(src.replace("a + 1", "a + 2"))
+    assert bench._code_only("int c = 6 / 2;  // half") == "int c = 6 / 2;"
