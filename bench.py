@@ -135,11 +135,12 @@ def _short(name):
 
 
 def _code_only(text):
-    """C++ source without its comments, trailing blanks and empty lines (the
-    hashed sources hold no comment markers inside string literals)."""
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    """C++ source without its comments and empty lines, each line's blanks
+    collapsed (the hashed sources hold no comment markers or runs of blanks
+    inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
-    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
 
 
 def _src_sha(fnames):
