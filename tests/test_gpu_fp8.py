@@ -135,14 +135,14 @@ def full_fp8():
 
 
 _fp8_cache = {}
-FP8_CASES = [("decode", 0), ("prefill", 0), ("prefill", 1)]
+FP8_CASES = [("decode", 0), ("prefill", 0), ("prefill", 1), ("skewed", 0)]
 FP8_CHUNK = 4096
 
 
 @pytest.mark.parametrize("name,chunk", FP8_CASES, ids=[f"{n}-{c}" for n, c in FP8_CASES])
 def test_fp8_full_shape(moe, full_fp8, name, chunk):
-    """Every token of the full-shape decode and prefill workloads (one GPU
-    run each; the oracle on chunks of FP8_CHUNK tokens)."""
+    """Every token of the full-shape decode, prefill and skewed (clamped)
+    workloads (one GPU run each; the oracle on chunks of FP8_CHUNK tokens)."""
     wl = synth.WORKLOADS[name]
     f8, f8dev = full_fp8
     if name not in _fp8_cache:
