@@ -695,6 +695,8 @@ def main():
     import sparse_moe_layer_fp32_amd as moe
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from sparse_moe_layer_fp32_amd import _build
+    _build.ensure_built()  # compiles only when nothing is built
     moe.load_library()
     head = args.config
     wl = synth.WORKLOADS[head]

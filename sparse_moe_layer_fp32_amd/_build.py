@@ -62,5 +62,14 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def ensure_built() -> str:
+    """libmoe.so as built; compiled first only when there is none (a fresh
+    checkout).  After a source change, build() again: this does not look at
+    the sources' dates."""
+    if not os.path.exists(LIB):
+        build(verbose=True)
+    return LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -42,3 +42,7 @@ _CONFIG = []
 @pytest.hookimpl(tryfirst=True)
 def pytest_sessionstart(session):
     _CONFIG.append(session.config)
+    # a fresh checkout has no libmoe.so: compile it once (the oracle and the
+    # input generator compile themselves on first use)
+    from sparse_moe_layer_fp32_amd import _build
+    _build.ensure_built()
